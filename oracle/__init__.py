@@ -1,0 +1,12 @@
+"""CPU oracle of the MoE FFN layer forward (float64 numpy) -- test infrastructure.
+
+Only the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU baseline leg may
+import this package. The GPU library never does and shares no code with it.
+"""
+from .moe_oracle import (SIGMOID, SOFTMAX, combine, expert_capacity, forward, gate_values,
+                         grouped_mlp, permute, route, router_logits, select_topk, shared_mlp,
+                         silu, swiglu_ffn, token_outputs)
+
+__all__ = ["SIGMOID", "SOFTMAX", "combine", "expert_capacity", "forward", "gate_values",
+           "grouped_mlp", "permute", "route", "router_logits", "select_topk", "shared_mlp",
+           "silu", "swiglu_ffn", "token_outputs"]

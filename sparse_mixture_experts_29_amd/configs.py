@@ -1,0 +1,105 @@
+"""Problem statements of the MoE FFN layer forward and the named synthetic workloads.
+
+A layer is described by the quantities the pages use for the problem: T tokens,
+model width d, expert width f, E routed experts, top-k, the gating function
+(softmax, or sigmoid renormalised over the chosen experts), a capacity factor
+(<= 0 means dropless) and optional always-on shared experts ("Mixture of Experts",
+shubhamtatvamasi.com, sections "The router" and "Load imbalance").
+
+The named workloads are the five shapes this library is checked and measured on.
+They hold shapes and seeds only; the values themselves come from ``inputs``.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+
+SOFTMAX = "softmax"
+SIGMOID = "sigmoid"
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    T: int
+    d_model: int
+    d_ff: int
+    n_experts: int
+    top_k: int
+    gating: str = SOFTMAX
+    capacity_factor: float = 0.0  # <= 0: dropless
+    n_shared: int = 0
+    d_ff_shared: int = 0
+    dtype: str = "bf16"  # "f32" or "bf16": dtype of x, every weight, and y
+    seed: int = 0
+    router_bias: str = "none"  # "none" | "zipf" | "normal"
+    bias_scale: float = 0.0  # zipf: exponent s; normal: std
+    x_stream: int = 0  # index of x's random stream (decode sweeps use T)
+
+    @property
+    def dropless(self) -> bool:
+        return not (self.capacity_factor > 0)
+
+    def replace(self, **kw) -> "LayerConfig":
+        return dataclasses.replace(self, **kw)
+
+    # --- algorithmic accounting (two FLOPs per multiply-add) -------------
+    def expert_flops_per_pair(self) -> int:
+        """gate, up and down projections of one routed (token, expert) pair."""
+        return 6 * self.d_model * self.d_ff
+
+    def shared_flops(self) -> int:
+        return 6 * self.d_model * self.d_ff_shared * self.T * self.n_shared
+
+    def router_flops(self) -> int:
+        return 2 * self.T * self.d_model * self.n_experts
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def expert_weight_bytes(self) -> int:
+        return 3 * self.d_model * self.d_ff * self.elem_bytes
+
+    def total_weight_bytes(self) -> int:
+        b = self.n_experts * self.expert_weight_bytes()
+        b += self.n_shared * 3 * self.d_model * self.d_ff_shared * self.elem_bytes
+        b += self.n_experts * self.d_model * self.elem_bytes
+        return b
+
+
+# Tiny fp32 layer: T=64, d=128, f=256, E=8, top-2, softmax, dropless.
+TINY_FP32 = LayerConfig("tiny_fp32_T64_d128_f256_E8_k2", T=64, d_model=128, d_ff=256,
+                        n_experts=8, top_k=2, dtype="f32", seed=0)
+# Mixtral-shaped prefill: T=4096, d=4096, f=14336, E=8, top-2, softmax, bf16.
+MIXTRAL_PREFILL = LayerConfig("mixtral_prefill_T4096_d4096_f14336_E8_k2", T=4096, d_model=4096,
+                              d_ff=14336, n_experts=8, top_k=2, seed=1)
+
+
+def mixtral_decode(T: int) -> LayerConfig:
+    """Mixtral-shaped low-batch decode layer; T in {1, 4, 16, 64} tokens per step."""
+    return LayerConfig(f"mixtral_decode_T{T}_d4096_f14336_E8_k2", T=T, d_model=4096,
+                       d_ff=14336, n_experts=8, top_k=2, seed=2, x_stream=T)
+
+
+DECODE_TS = (1, 4, 16, 64)
+
+# Fine-grained Qwen3-30B-A3B-style layer: T=8192, d=2048, f=768, E=128, top-8, Zipf-skewed
+# router bias; run dropless and with capacity factor 1.25.
+QWEN3_FINE = LayerConfig("qwen3_fine_T8192_d2048_f768_E128_k8", T=8192, d_model=2048, d_ff=768,
+                         n_experts=128, top_k=8, seed=3, router_bias="zipf", bias_scale=1.1)
+QWEN3_FINE_CF = QWEN3_FINE.replace(name="qwen3_fine_cf1.25_T8192_d2048_f768_E128_k8",
+                                   capacity_factor=1.25)
+# DeepSeek-V3-style layer: T=16384, d=7168, f=2048, E=256, top-8, sigmoid, 1 shared expert.
+DEEPSEEK_V3 = LayerConfig("deepseek_v3_T16384_d7168_f2048_E256_k8_s1", T=16384, d_model=7168,
+                          d_ff=2048, n_experts=256, top_k=8, gating=SIGMOID, n_shared=1,
+                          d_ff_shared=2048, seed=4, router_bias="normal", bias_scale=0.5)
+
+ALL = {c.name: c for c in [TINY_FP32, MIXTRAL_PREFILL, *[mixtral_decode(t) for t in DECODE_TS],
+                           QWEN3_FINE, QWEN3_FINE_CF, DEEPSEEK_V3]}
+
+
+def reduced(cfg: LayerConfig, **kw) -> LayerConfig:
+    """Same structure (gating, skew recipe, shared experts, capacity) at a smaller size."""
+    name = cfg.name.split("_T")[0] + "_reduced_" + "_".join(f"{k}{v}" for k, v in sorted(kw.items()))
+    return cfg.replace(name=name, **kw)

@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs for the MoE layer: activations, router, experts.
+
+This module is shared by the tests, the benchmark and the oracle's callers. It holds
+no arithmetic of the layer itself: it only draws numbers and stores them.
+
+Recipe (every tensor has its own numpy PCG64 stream ``default_rng([seed, tag, index])``
+so that experts can be produced one at a time and regenerated on demand):
+
+* draws are float32 N(0, 1) scaled by the tensor's std, then (bf16 workloads) rounded
+  to bfloat16 with round-to-nearest-even and kept as uint16 bit patterns;
+* x ~ N(0, 1); router, gate and up weights std 1/sqrt(d); down weights std 1/sqrt(f)
+  (std = 1/sqrt(fan_in));
+* router bias: none; "zipf" = a seeded permutation gives each expert a rank r in 1..E,
+  w = r^-s, and the bias is w min-max scaled linearly onto [-2, 2]; "normal" = N(0, std).
+
+Memory layout of every weight is out-features-major (the layout of a linear layer's
+weight): router [E][d], gate and up [E][f][d], down [E][d][f], shared gate/up
+[n_s][f_s][d], shared down [n_s][d][f_s]. The matrix products are the ones of the
+row-vector convention y = x . W with W = stored^T.
+"""
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+from typing import Callable, Optional
+
+import numpy as np
+
+from .configs import LayerConfig
+
+TAG_X, TAG_WR, TAG_BIAS, TAG_WG, TAG_WU, TAG_WD, TAG_SWG, TAG_SWU, TAG_SWD, TAG_PERM = range(10)
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).copy()
+    b += np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    return (b >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> the float32 values they denote (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(seed: int, tag: int, index: int, shape, std: float) -> np.ndarray:
+    a = np.random.default_rng([seed, tag, index]).standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return a
+
+
+@dataclass
+class LayerInputs:
+    """Host-side inputs of one layer. ``storage`` arrays are what is uploaded
+    (uint16 bf16 bits or float32); ``values(...)`` gives their exact float32 values."""
+    cfg: LayerConfig
+    x: np.ndarray  # [T, d] storage
+    w_router: np.ndarray  # [E, d] storage
+    router_bias: Optional[np.ndarray]  # [E] float32 or None
+
+    def _store(self, a32: np.ndarray) -> np.ndarray:
+        return to_bf16_bits(a32) if self.cfg.dtype == "bf16" else a32
+
+    def values(self, storage: np.ndarray) -> np.ndarray:
+        return bf16_bits_to_f32(storage) if self.cfg.dtype == "bf16" else storage
+
+    # ---- routed experts ------------------------------------------------
+    def expert(self, e: int):
+        c = self.cfg
+        sd, sf = 1.0 / math.sqrt(c.d_model), 1.0 / math.sqrt(c.d_ff)
+        wg = self._store(_normal(c.seed, TAG_WG, e, (c.d_ff, c.d_model), sd))
+        wu = self._store(_normal(c.seed, TAG_WU, e, (c.d_ff, c.d_model), sd))
+        wd = self._store(_normal(c.seed, TAG_WD, e, (c.d_model, c.d_ff), sf))
+        return wg, wu, wd
+
+    def expert_values(self, e: int):
+        return tuple(self.values(w) for w in self.expert(e))
+
+    # ---- shared experts ------------------------------------------------
+    def shared(self, s: int):
+        c = self.cfg
+        sd, sf = 1.0 / math.sqrt(c.d_model), 1.0 / math.sqrt(c.d_ff_shared)
+        wg = self._store(_normal(c.seed, TAG_SWG, s, (c.d_ff_shared, c.d_model), sd))
+        wu = self._store(_normal(c.seed, TAG_SWU, s, (c.d_ff_shared, c.d_model), sd))
+        wd = self._store(_normal(c.seed, TAG_SWD, s, (c.d_model, c.d_ff_shared), sf))
+        return wg, wu, wd
+
+    def shared_values(self, s: int):
+        return tuple(self.values(w) for w in self.shared(s))
+
+    # ---- bulk production ---------------------------------------------
+    def for_each_expert(self, fn: Callable[[int, tuple], None], threads: int = 8,
+                        shared: bool = False) -> None:
+        """Call fn(index, (wg, wu, wd)) for every routed (or shared) expert, producing
+        them on ``threads`` threads (numpy releases the GIL while drawing)."""
+        n = self.cfg.n_shared if shared else self.cfg.n_experts
+        make = self.shared if shared else self.expert
+
+        def work(i):
+            fn(i, make(i))
+
+        if threads <= 1 or n <= 1:
+            for i in range(n):
+                work(i)
+            return
+        with ThreadPoolExecutor(max_workers=min(threads, n)) as ex:
+            list(ex.map(work, range(n)))
+
+    def stacked_experts(self, threads: int = 8):
+        """All routed experts as three stacked storage arrays [E,f,d], [E,f,d], [E,d,f]."""
+        c = self.cfg
+        dt = np.uint16 if c.dtype == "bf16" else np.float32
+        wg = np.empty((c.n_experts, c.d_ff, c.d_model), dt)
+        wu = np.empty_like(wg)
+        wd = np.empty((c.n_experts, c.d_model, c.d_ff), dt)
+
+        def put(e, w):
+            wg[e], wu[e], wd[e] = w
+
+        self.for_each_expert(put, threads)
+        return wg, wu, wd
+
+    def stacked_shared(self):
+        c = self.cfg
+        if c.n_shared == 0:
+            return None
+        dt = np.uint16 if c.dtype == "bf16" else np.float32
+        wg = np.empty((c.n_shared, c.d_ff_shared, c.d_model), dt)
+        wu = np.empty_like(wg)
+        wd = np.empty((c.n_shared, c.d_model, c.d_ff_shared), dt)
+        for s in range(c.n_shared):
+            wg[s], wu[s], wd[s] = self.shared(s)
+        return wg, wu, wd
+
+
+def router_bias_values(cfg: LayerConfig) -> Optional[np.ndarray]:
+    E = cfg.n_experts
+    if cfg.router_bias == "none":
+        return None
+    if cfg.router_bias == "zipf":
+        rank = np.random.default_rng([cfg.seed, TAG_PERM, 0]).permutation(E).astype(np.float64) + 1.0
+        w = rank ** (-cfg.bias_scale)
+        return (4.0 * (w - w.min()) / (w.max() - w.min()) - 2.0).astype(np.float32)
+    if cfg.router_bias == "normal":
+        return _normal(cfg.seed, TAG_BIAS, 0, (E,), cfg.bias_scale)
+    raise ValueError(f"unknown router bias recipe {cfg.router_bias!r}")
+
+
+def make_inputs(cfg: LayerConfig) -> LayerInputs:
+    """Activations, router weight and bias of ``cfg`` (experts are produced on demand)."""
+    store = to_bf16_bits if cfg.dtype == "bf16" else (lambda a: a)
+    x = store(_normal(cfg.seed, TAG_X, cfg.x_stream, (cfg.T, cfg.d_model), 1.0))
+    wr = store(_normal(cfg.seed, TAG_WR, 0, (cfg.n_experts, cfg.d_model), 1.0 / math.sqrt(cfg.d_model)))
+    return LayerInputs(cfg, x, wr, router_bias_values(cfg))
