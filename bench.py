@@ -1,0 +1,217 @@
+"""Benchmark of the MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one moe_layer_forward (route, permute, grouped gate/up + SiLU*mul GEMM,
+grouped down GEMM, combine) over the workload's seeded synthetic batch, all inputs
+resident in HBM. The default workload is the Mixtral-shaped prefill layer (T=4096,
+d=4096, f=14336, E=8, top-2, bf16). Prints ONE JSON line (rank 0):
+  value      routed tokens per second (T * K / elapsed over the K timed steps)
+  roofline   the gated grouped GEMM (the dominant kernel): algorithmic FLOPs per launch
+             (4 d f N_kept) / its average launch time, HIP events recorded around that
+             launch on the layer's stream inside the timed steps, against 2.5 PFLOP/s
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+METRIC = "routed tokens/sec per MoE layer; % of bf16 MFMA peak (prefill) / HBM peak (decode)"
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime (recorded by libmoe on its launch stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> ctypes.c_void_p:
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.hip.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def kernel_source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "sparse_mixture_experts_29_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current source of the kernel; otherwise None."""
+    p = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        rec = d.get(workload)
+        if rec and rec.get("source_sha256_16") == kernel_source_hash(kernel_file):
+            return rec.get("hbm_bytes_per_launch")
+    except (ValueError, OSError):
+        return None
+    return None
+
+
+def cpu_baseline(li, n_tokens: int):
+    """The oracle (as it stands) on the first n_tokens of the workload, on host cores."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    c = li.cfg
+    x = li.values(li.x[:n_tokens])
+    wr = li.values(li.w_router)
+    experts = [li.expert_values(e) for e in range(c.n_experts)]  # input generation: untimed
+    shared = [li.shared_values(s) for s in range(c.n_shared)]
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    oracle.forward(x, wr, li.router_bias, top_k=c.top_k, gating=c.gating,
+                   capacity_factor=c.capacity_factor, experts=experts, shared=shared,
+                   n_shared=c.n_shared)
+    dt = time.perf_counter() - t0
+    del experts
+    return dict(value=n_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"first {n_tokens} of {c.T} tokens of {c.name}, all {c.n_experts} experts' "
+                       f"weights widened to float64 inside the timed region; {dt:.1f} s",
+                seconds=round(dt, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="name of a configs.ALL entry")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(expert parallelism is a design note only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_29_amd import binding, configs
+    from sparse_mixture_experts_29_amd.device import DeviceLayer
+    from sparse_mixture_experts_29_amd.inputs import make_inputs
+
+    cfg = configs.ALL[args.workload] if args.workload else configs.MIXTRAL_PREFILL
+    binding.load_library()
+    li = make_inputs(cfg)
+    t_gen = time.perf_counter()
+    dev = DeviceLayer(li, device="cuda:0", threads=16)
+    print(f"# inputs resident in HBM ({cfg.total_weight_bytes() / 1e9:.2f} GB weights) "
+          f"in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    # routing statistics of this batch (outside the timed region)
+    b = dev.stage_buffers()
+    dev.route(b, logits=False)
+    dev.permute(b)
+    torch.cuda.synchronize()
+    counts = b["counts"].cpu().numpy()
+    n_kept = int(b["offsets"][-1].item())
+    touched = int((counts > 0).sum())
+    del b
+
+    ev = HipEvents()
+    for _ in range(args.warmup):
+        dev.forward()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    begins = [ev.create() for _ in range(K)]
+    ends = [ev.create() for _ in range(K)]
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_ev[0].record(stream)
+    for i in range(K):
+        binding.moe_time_next_launch(binding.MOE_KERNEL_GATE_UP, begins[i], ends[i])
+        dev.forward()
+        step_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(K)])
+    gate_up_ms = np.array([ev.elapsed_ms(begins[i], ends[i]) for i in range(K)])
+    for e in begins + ends:
+        ev.destroy(e)
+
+    value = cfg.T * K / elapsed
+    flops_gate_up = 4.0 * cfg.d_model * cfg.d_ff * n_kept + 4.0 * cfg.d_model * cfg.d_ff_shared * cfg.T * cfg.n_shared
+    achieved = flops_gate_up / (gate_up_ms.mean() * 1e-3) / 1e12
+    layer_flops = (cfg.expert_flops_per_pair() * n_kept + cfg.shared_flops() + cfg.router_flops())
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) random-init weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
+                   "n_experts": cfg.n_experts, "top_k": cfg.top_k, "gating": cfg.gating,
+                   "capacity_factor": cfg.capacity_factor, "n_shared": cfg.n_shared,
+                   "d_ff_shared": cfg.d_ff_shared, "parallelism": "single GPU"},
+        "roofline": {
+            "kernel": "grouped_gemm_bf16<gated> (gate/up GEMM + SiLU*mul)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_from_profile("grouped_mlp.hip", cfg.name),
+            "avg_launch_ms": round(float(gate_up_ms.mean()), 4),
+            "flops_per_launch": flops_gate_up,
+        },
+        "layer": {
+            "step_ms_p50": round(float(np.percentile(step_ms, 50)), 4),
+            "step_ms_p95": round(float(np.percentile(step_ms, 95)), 4),
+            "step_ms_p99": round(float(np.percentile(step_ms, 99)), 4),
+            "layer_tflops": round(layer_flops / (np.median(step_ms) * 1e-3) / 1e12, 2),
+            "layer_mfma_frac": round(layer_flops / (np.median(step_ms) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "n_kept": n_kept,
+            "experts_touched": touched,
+            "max_over_mean_load": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
+        },
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(li, min(args.cpu_tokens, cfg.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts FFN layer forward.
+ *
+ * One MoE layer on one GPU, in the steps the pages give for it:
+ *   router linear layer -> softmax or sigmoid scores -> top-k -> gates renormalised over
+ *   the chosen k -> permute tokens by destination expert (dropless, or with a capacity
+ *   limit whose overflow is dropped to the residual path) -> each expert's SwiGLU MLP as
+ *   a grouped GEMM over its batch (+ optional always-on shared experts) -> undo the
+ *   permutation with a gate-weighted combine.
+ * Sources: shubhamtatvamasi.com/llm-inference/moe "Mixture of Experts" (sections "The
+ * router", "Load imbalance", Q&A "How does a top-k router work?" and "What are capacity
+ * factor and token dropping ..."); klaylearn.com/glossary/mixture-of-experts (definition:
+ * permute by destination expert, grouped GEMMs per expert batch, undo the permutation);
+ * shipai.vats.cc "Mixture of Experts (MoE)" section "How routing works (intuition)".
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except `cfg` and the
+ *    out-parameters of moe_workspace_size / moe_capacity, which are host pointers.
+ *    The library allocates no memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work on it:
+ *    they are asynchronous, never synchronise the host, and never copy data back.
+ *    Calls on different streams with disjoint outputs and workspaces may overlap.
+ *  - Element type of x, every weight, y_perm, y_shared and y is cfg->dtype
+ *    (MOE_F32: float; MOE_BF16: bfloat16 bit patterns). Accumulation is fp32.
+ *    Router bias and gates are float; indices are int32.
+ *  - Layouts are row-major and contiguous. Weights are stored out-features-major, the
+ *    layout of a linear layer's weight, i.e. the TRANSPOSE of the d x f matrices of the
+ *    row-vector form y = x . W:
+ *      x [T][d]   w_router [E][d]   w_gate, w_up [E][f][d]   w_down [E][d][f]
+ *      shared: ws_gate, ws_up [n_shared][f_s][d]   ws_down [n_shared][d][f_s]
+ *  - Errors are returned before anything is enqueued: MOE_ERR_INVALID_ARG for an
+ *    inconsistent config or a NULL required pointer, MOE_ERR_UNSUPPORTED for sizes the
+ *    kernels do not tile (see moe_config), MOE_ERR_WORKSPACE for a workspace smaller
+ *    than moe_workspace_size. MOE_ERR_HIP reports a failed launch; faults inside a
+ *    kernel surface at the caller's next synchronisation. T = 0 is a no-op (MOE_OK).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };       /* moe_config.dtype */
+enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 }; /* moe_config.gating */
+enum { MOE_OP_PERMUTE = 0, MOE_OP_GROUPED_MLP = 1, MOE_OP_LAYER = 2 }; /* workspace users */
+
+/* The problem statement of one layer (the pages' T tokens, d_model, d_ff, E experts,
+ * top-k, gating function, capacity factor and shared experts).
+ * Limits: 1 <= top_k <= min(E, 32); 1 <= E <= 1024; d_model and d_ff (and d_ff_shared)
+ * multiples of 64; T < 2^31 / top_k. capacity_factor <= 0 means dropless; otherwise each
+ * expert keeps at most C = ceil(capacity_factor * T * top_k / E) (token, expert) pairs,
+ * the ones with the lowest token index, evaluated in double precision. */
+typedef struct moe_config {
+  int64_t T;              /* tokens in this call */
+  int32_t d_model;        /* d */
+  int32_t d_ff;           /* f: width of each routed expert */
+  int32_t n_experts;      /* E */
+  int32_t top_k;          /* k */
+  int32_t gating;         /* MOE_SOFTMAX or MOE_SIGMOID */
+  float capacity_factor;  /* <= 0: dropless; must be finite */
+  int32_t n_shared;       /* shared experts every token visits (weight 1) */
+  int32_t d_ff_shared;    /* f_s (ignored when n_shared == 0) */
+  int32_t dtype;          /* MOE_F32 or MOE_BF16 */
+  int32_t reserved;       /* must be 0 */
+} moe_config;
+
+/* Human-readable name of a status code (static string, never NULL). */
+MOE_API const char* moe_status_string(int status);
+
+/* Validates cfg (as every entry point does). */
+MOE_API moe_status moe_check_config(const moe_config* cfg);
+
+/* Per-expert capacity C (capacity mode) or -1 (dropless), into *capacity (host). */
+MOE_API moe_status moe_capacity(const moe_config* cfg, int64_t* capacity);
+
+/* Upper bound on kept (token, expert) pairs: T*k dropless, min(T*k, E*C) otherwise.
+ * This is the row count of sorted_slot and y_perm. Written into *max_kept (host). */
+MOE_API moe_status moe_max_kept(const moe_config* cfg, int64_t* max_kept);
+
+/* Bytes of device workspace `op` (MOE_OP_*) needs for cfg, into *bytes (host). */
+MOE_API moe_status moe_workspace_size(const moe_config* cfg, int op, size_t* bytes);
+
+/* Router (pages: "The router"; Q&A "How does a top-k router work?").
+ *   logits[t][e] = sum_i x[t][i] * w_router[e][i] + router_bias[e]   (fp32 accumulate)
+ *   topk_idx[t][j], j < k: the k largest logits, descending, ties to the lower index;
+ *   topk_gate[t][j]: softmax over the chosen logits (= softmax over all E renormalised
+ *   over the chosen k), or sigmoid(l) / sum of the chosen sigmoid(l) for MOE_SIGMOID.
+ * router_bias [E] float may be NULL (no bias). logits [T][E] float may be NULL. */
+MOE_API moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* router_bias, int32_t* topk_idx, float* topk_gate,
+                     float* logits, void* stream);
+
+/* Permute (klaylearn "Mixture of Experts" definition; pages' "Load imbalance").
+ * Pair s = t*k + j goes to expert topk_idx[s]. Pairs are grouped by expert, and within an
+ * expert ordered by ascending token; with a capacity C only the first C of each expert
+ * are kept. Outputs (int32 unless noted):
+ *   counts[E]          pairs routed to each expert before dropping
+ *   offsets[E+1]       exclusive prefix sum of kept pairs; offsets[E] = N_kept
+ *   sorted_slot[max_kept]  s of the kept pairs in grouped order; entries >= N_kept are -1
+ *   pos[T*k]           index of pair s in the grouped order, -1 if dropped
+ *   drop_mask[T*k]     uint8, 1 if pair s was dropped
+ * Deterministic (bit-identical on every call). Needs ws of MOE_OP_PERMUTE bytes. */
+MOE_API moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_slot, int32_t* pos, uint8_t* drop_mask,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped expert MLP (klaylearn: "grouped GEMMs on each expert's batch"; techbonafide
+ * "Experts as Specialized Subnetworks": an expert is a feed-forward block). For every
+ * routed expert e and grouped position p in [offsets[e], offsets[e+1]):
+ *   v = x[sorted_slot[p] / k];  y_perm[p] = (silu(v . Wg_e) * (v . Wu_e)) . Wd_e
+ * and for every shared expert s and token t (pages' "The router": shared experts every
+ * token always visits):  y_shared[s][t] = (silu(x_t . Wg_s) * (x_t . Wu_s)) . Wd_s.
+ * y_perm [max_kept][d]; y_shared [n_shared][T][d] (required iff n_shared > 0, as are
+ * ws_gate/ws_up/ws_down). The intermediate silu(.)*(.) is rounded to dtype.
+ * Needs ws of MOE_OP_GROUPED_MLP bytes. */
+MOE_API moe_status moe_grouped_mlp(const moe_config* cfg, const void* x, const int32_t* sorted_slot,
+                           const int32_t* offsets, const void* w_gate, const void* w_up,
+                           const void* w_down, const void* ws_gate, const void* ws_up,
+                           const void* ws_down, void* y_perm, void* y_shared, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Combine (pages' Q&A "How does a top-k router work?": the gate-weighted sum; klaylearn:
+ * undo the permutation):
+ *   y[t] = sum over j < k with pos[t*k+j] >= 0 of topk_gate[t*k+j] * y_perm[pos[t*k+j]]
+ *          + sum over s of y_shared[s][t]
+ * in fp32, j ascending, rounded once to dtype. A dropped pair adds nothing (the residual
+ * add is the caller's). y_shared may be NULL when n_shared == 0. */
+MOE_API moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* pos,
+                       const float* topk_gate, const void* y_shared, void* y, void* stream);
+
+/* The whole layer: moe_route, moe_permute, moe_grouped_mlp and moe_combine on one stream,
+ * intermediates in ws (MOE_OP_LAYER bytes). y [T][d]. Same results as the four calls. */
+MOE_API moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* router_bias, const void* w_gate, const void* w_up,
+                             const void* w_down, const void* ws_gate, const void* ws_up,
+                             const void* ws_down, void* y, void* ws, size_t ws_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,178 @@
+"""Thin ctypes binding of libmoe.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls (declared in include/moe.h) and
+takes torch tensors that already live on the GPU; it passes their device pointers, the
+layer's moe_config and the current HIP stream, and turns a non-zero status into
+``MoeError``. Every step of the computation runs in the library's HIP kernels. If the
+library has not been built, the first call raises ``MoeLibraryMissing``; there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+from .configs import SIGMOID, LayerConfig
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_OP_PERMUTE, MOE_OP_GROUPED_MLP, MOE_OP_LAYER = 0, 1, 2
+
+# every function the header declares
+EXPORTS = ("moe_status_string", "moe_check_config", "moe_capacity", "moe_max_kept",
+           "moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_mlp", "moe_combine",
+           "moe_layer_forward")
+
+
+class MoeLibraryMissing(RuntimeError):
+    pass
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)}")
+        self.status = status
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("gating", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float), ("n_shared", ctypes.c_int32),
+                ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_C = ctypes.POINTER(MoeConfig)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Open libmoe.so (once) and declare the argument types of every entry point."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise MoeLibraryMissing(
+            f"{path} is not built; run `python -m sparse_mixture_experts_29_amd.build` "
+            "(the MoE layer has no other implementation)")
+    lib = ctypes.CDLL(path)
+    sz = ctypes.c_size_t
+    sig = {
+        "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_check_config": (ctypes.c_int, [_C]),
+        "moe_capacity": (ctypes.c_int, [_C, ctypes.POINTER(ctypes.c_int64)]),
+        "moe_max_kept": (ctypes.c_int, [_C, ctypes.POINTER(ctypes.c_int64)]),
+        "moe_workspace_size": (ctypes.c_int, [_C, ctypes.c_int, ctypes.POINTER(sz)]),
+        "moe_route": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_permute": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "moe_grouped_mlp": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "moe_combine": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P]),
+        "moe_layer_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_status_string(int(status)).decode()
+
+
+def make_config(cfg: LayerConfig, T: Optional[int] = None) -> MoeConfig:
+    return MoeConfig(T=cfg.T if T is None else T, d_model=cfg.d_model, d_ff=cfg.d_ff,
+                     n_experts=cfg.n_experts, top_k=cfg.top_k,
+                     gating=MOE_SIGMOID if cfg.gating == SIGMOID else MOE_SOFTMAX,
+                     capacity_factor=float(cfg.capacity_factor), n_shared=cfg.n_shared,
+                     d_ff_shared=cfg.d_ff_shared if cfg.n_shared else 0,
+                     dtype=MOE_BF16 if cfg.dtype == "bf16" else MOE_F32, reserved=0)
+
+
+def _cfg(c) -> MoeConfig:
+    return make_config(c) if isinstance(c, LayerConfig) else c
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+# ------------------------------------------------------------------ queries
+def moe_check_config(cfg) -> int:
+    return load_library().moe_check_config(ctypes.byref(_cfg(cfg)))
+
+
+def moe_capacity(cfg) -> int:
+    v = ctypes.c_int64()
+    _check(load_library().moe_capacity(ctypes.byref(_cfg(cfg)), ctypes.byref(v)), "moe_capacity")
+    return v.value
+
+
+def moe_max_kept(cfg) -> int:
+    v = ctypes.c_int64()
+    _check(load_library().moe_max_kept(ctypes.byref(_cfg(cfg)), ctypes.byref(v)), "moe_max_kept")
+    return v.value
+
+
+def moe_workspace_size(cfg, op: int) -> int:
+    v = ctypes.c_size_t()
+    _check(load_library().moe_workspace_size(ctypes.byref(_cfg(cfg)), op, ctypes.byref(v)),
+           "moe_workspace_size")
+    return v.value
+
+
+# ------------------------------------------------------------------ the steps
+def moe_route(cfg, x, w_router, router_bias, topk_idx, topk_gate, logits=None, stream=None):
+    _check(load_library().moe_route(ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                    _ptr(topk_idx), _ptr(topk_gate), _ptr(logits), _stream(stream)),
+           "moe_route")
+
+
+def moe_permute(cfg, topk_idx, counts, offsets, sorted_slot, pos, drop_mask, ws, stream=None):
+    _check(load_library().moe_permute(ctypes.byref(_cfg(cfg)), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                                      _ptr(sorted_slot), _ptr(pos), _ptr(drop_mask), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_permute")
+
+
+def moe_grouped_mlp(cfg, x, sorted_slot, offsets, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                    y_perm, y_shared, ws, stream=None):
+    _check(load_library().moe_grouped_mlp(
+        ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(sorted_slot), _ptr(offsets), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y_perm), _ptr(y_shared), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "moe_grouped_mlp")
+
+
+def moe_combine(cfg, y_perm, pos, topk_gate, y_shared, y, stream=None):
+    _check(load_library().moe_combine(ctypes.byref(_cfg(cfg)), _ptr(y_perm), _ptr(pos), _ptr(topk_gate),
+                                      _ptr(y_shared), _ptr(y), _stream(stream)), "moe_combine")
+
+
+def moe_layer_forward(cfg, x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                      y, ws, stream=None):
+    _check(load_library().moe_layer_forward(
+        ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward")

@@ -1,0 +1,66 @@
+// Shared device helpers and the internal launch interface of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// fp32 -> bf16, round to nearest even (finite values; NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float sigmoid_f32(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// Internal view of moe_config with derived quantities (host-computed).
+struct Shape {
+  int64_t T;
+  int d, f, E, k, gating, n_shared, f_s, dtype;
+  int64_t capacity;  // -1: dropless
+  int64_t max_kept;  // rows of sorted_slot / y_perm
+};
+
+// Workspace of the permute step: per-chunk expert counts.
+constexpr int kPermuteChunk = 1024;  // (token, slot) pairs per chunk (one wave walks one chunk)
+int64_t permute_chunks(const Shape& s);
+size_t permute_ws_bytes(const Shape& s);
+
+// Grouped MLP: tile table + intermediate activations.
+size_t grouped_ws_bytes(const Shape& s);
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_route(const Shape& s, const void* x, const void* w_router, const float* bias,
+                        int32_t* idx, float* gate, float* logits, hipStream_t st);
+hipError_t launch_permute(const Shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_slot, int32_t* pos, uint8_t* drop, void* ws,
+                          hipStream_t st);
+hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sorted_slot,
+                              const int32_t* offsets, const void* wg, const void* wu,
+                              const void* wd, const void* swg, const void* swu, const void* swd,
+                              void* y_perm, void* y_shared, void* ws, hipStream_t st);
+hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos,
+                          const float* gate, const void* y_shared, void* y, hipStream_t st);
+
+inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace moe

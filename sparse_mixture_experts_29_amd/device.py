@@ -1,0 +1,127 @@
+"""Device-resident layer: uploads a layer's inputs once and owns its outputs and workspace.
+
+Plumbing for callers of the binding (tests, benchmark, smoke run): torch allocates the
+device memory, the library computes. Weights are uploaded expert by expert while other
+threads draw the next experts, so a 22.6 GB layer never sits whole in host memory.
+"""
+from __future__ import annotations
+
+import threading
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding
+from .configs import LayerConfig
+from .inputs import LayerInputs
+
+
+def torch_dtype(cfg: LayerConfig):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def host_to_device(a: np.ndarray, cfg: LayerConfig, device) -> torch.Tensor:
+    """Upload a storage array (uint16 bf16 bits or float32) as a bf16/fp32 device tensor."""
+    if cfg.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+
+def device_to_host_f32(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+class DeviceLayer:
+    def __init__(self, li: LayerInputs, device: str = "cuda:0", threads: int = 8,
+                 weights_from: Optional["DeviceLayer"] = None):
+        """weights_from: reuse the expert weights already uploaded for another layer of the
+        same shape and seed (e.g. the same layer at another token count)."""
+        cfg = li.cfg
+        self.cfg, self.inputs, self.device = cfg, li, torch.device(device)
+        dt = torch_dtype(cfg)
+        E, d, f = cfg.n_experts, cfg.d_model, cfg.d_ff
+        self.x = host_to_device(li.x, cfg, device)
+        self.w_router = host_to_device(li.w_router, cfg, device)
+        self.router_bias = None if li.router_bias is None else torch.from_numpy(li.router_bias).to(device)
+        if weights_from is not None:
+            o = weights_from.cfg
+            assert (o.seed, o.n_experts, o.d_model, o.d_ff, o.dtype) == (cfg.seed, E, d, f, cfg.dtype)
+            self.w_gate, self.w_up, self.w_down = weights_from.w_gate, weights_from.w_up, weights_from.w_down
+        else:
+            self.w_gate = torch.empty((E, f, d), dtype=dt, device=device)
+            self.w_up = torch.empty((E, f, d), dtype=dt, device=device)
+            self.w_down = torch.empty((E, d, f), dtype=dt, device=device)
+            lock = threading.Lock()
+
+            def put(e, w):
+                with lock:
+                    self.w_gate[e].copy_(host_to_device(w[0], cfg, device))
+                    self.w_up[e].copy_(host_to_device(w[1], cfg, device))
+                    self.w_down[e].copy_(host_to_device(w[2], cfg, device))
+
+            li.for_each_expert(put, threads)
+        self.ws_gate = self.ws_up = self.ws_down = None
+        if cfg.n_shared:
+            fs = cfg.d_ff_shared
+            self.ws_gate = torch.empty((cfg.n_shared, fs, d), dtype=dt, device=device)
+            self.ws_up = torch.empty((cfg.n_shared, fs, d), dtype=dt, device=device)
+            self.ws_down = torch.empty((cfg.n_shared, d, fs), dtype=dt, device=device)
+            for s in range(cfg.n_shared):
+                w = li.shared(s)
+                self.ws_gate[s].copy_(host_to_device(w[0], cfg, device))
+                self.ws_up[s].copy_(host_to_device(w[1], cfg, device))
+                self.ws_down[s].copy_(host_to_device(w[2], cfg, device))
+        self.y = torch.empty((cfg.T, d), dtype=dt, device=device)
+        self.ws = torch.empty(binding.moe_workspace_size(cfg, binding.MOE_OP_LAYER), dtype=torch.uint8,
+                              device=device)
+        torch.cuda.synchronize(self.device)
+
+    # ---------------------------------------------------------------- whole layer
+    def forward(self, stream=None) -> torch.Tensor:
+        binding.moe_layer_forward(self.cfg, self.x, self.w_router, self.router_bias, self.w_gate,
+                                  self.w_up, self.w_down, self.ws_gate, self.ws_up, self.ws_down,
+                                  self.y, self.ws, stream)
+        return self.y
+
+    # ---------------------------------------------------------------- step by step
+    def stage_buffers(self) -> dict:
+        cfg, dev = self.cfg, self.device
+        pairs = cfg.T * cfg.top_k
+        mk = binding.moe_max_kept(cfg)
+        dt = torch_dtype(cfg)
+        b = dict(
+            idx=torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev),
+            gate=torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev),
+            logits=torch.empty((cfg.T, cfg.n_experts), dtype=torch.float32, device=dev),
+            counts=torch.empty(cfg.n_experts, dtype=torch.int32, device=dev),
+            offsets=torch.empty(cfg.n_experts + 1, dtype=torch.int32, device=dev),
+            sorted_slot=torch.empty(mk, dtype=torch.int32, device=dev),
+            pos=torch.empty(pairs, dtype=torch.int32, device=dev),
+            drop=torch.empty(pairs, dtype=torch.uint8, device=dev),
+            permute_ws=torch.empty(max(1, binding.moe_workspace_size(cfg, binding.MOE_OP_PERMUTE)),
+                                   dtype=torch.uint8, device=dev),
+            grouped_ws=torch.empty(max(1, binding.moe_workspace_size(cfg, binding.MOE_OP_GROUPED_MLP)),
+                                   dtype=torch.uint8, device=dev),
+            y_perm=torch.empty((mk, cfg.d_model), dtype=dt, device=dev),
+            y_shared=(torch.empty((cfg.n_shared, cfg.T, cfg.d_model), dtype=dt, device=dev)
+                      if cfg.n_shared else None),
+            y=torch.empty((cfg.T, cfg.d_model), dtype=dt, device=dev),
+        )
+        return b
+
+    def route(self, b: dict, logits: bool = True, stream=None):
+        binding.moe_route(self.cfg, self.x, self.w_router, self.router_bias, b["idx"], b["gate"],
+                          b["logits"] if logits else None, stream)
+
+    def permute(self, b: dict, idx: Optional[torch.Tensor] = None, stream=None):
+        binding.moe_permute(self.cfg, b["idx"] if idx is None else idx, b["counts"], b["offsets"],
+                            b["sorted_slot"], b["pos"], b["drop"], b["permute_ws"], stream)
+
+    def grouped_mlp(self, b: dict, stream=None):
+        binding.moe_grouped_mlp(self.cfg, self.x, b["sorted_slot"], b["offsets"], self.w_gate, self.w_up,
+                                self.w_down, self.ws_gate, self.ws_up, self.ws_down, b["y_perm"],
+                                b["y_shared"], b["grouped_ws"], stream)
+
+    def combine(self, b: dict, stream=None):
+        binding.moe_combine(self.cfg, b["y_perm"], b["pos"], b["gate"], b["y_shared"], b["y"], stream)
