@@ -61,6 +61,13 @@ typedef enum {
 enum { MOE_F32 = 0, MOE_BF16 = 1 };       /* moe_config.dtype */
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 }; /* moe_config.gating */
 enum { MOE_OP_PERMUTE = 0, MOE_OP_GROUPED_MLP = 1, MOE_OP_LAYER = 2 }; /* workspace users */
+enum { /* kernels that moe_time_next_launch can bracket */
+  MOE_KERNEL_ROUTER = 0,
+  MOE_KERNEL_PERMUTE_SCATTER = 1,
+  MOE_KERNEL_GATE_UP = 2, /* grouped gate/up GEMM with the SiLU*mul epilogue */
+  MOE_KERNEL_DOWN = 3,    /* grouped down GEMM */
+  MOE_KERNEL_COMBINE = 4
+};
 
 /* The problem statement of one layer (the pages' T tokens, d_model, d_ff, E experts,
  * top-k, gating function, capacity factor and shared experts).
@@ -153,6 +160,13 @@ MOE_API moe_status moe_layer_forward(const moe_config* cfg, const void* x, const
                              const void* w_down, const void* ws_gate, const void* ws_up,
                              const void* ws_down, void* y, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* Instrumentation, for measuring one kernel inside a layer call. The next launch of
+ * `kernel` (MOE_KERNEL_*) made by any entry point called on THIS host thread is bracketed
+ * by hipEventRecord(begin_event) and hipEventRecord(end_event) on that call's stream;
+ * then the request is cleared. begin_event / end_event are hipEvent_t created by the
+ * caller. A new request replaces a pending one; kernel = -1 cancels it. */
+MOE_API moe_status moe_time_next_launch(int kernel, void* begin_event, void* end_event);
 
 #ifdef __cplusplus
 }

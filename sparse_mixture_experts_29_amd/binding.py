@@ -15,17 +15,20 @@ from typing import Optional
 
 from .configs import SIGMOID, LayerConfig
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# the in-tree build; MOE_LIB may name another build of the same sources (for A/B timing)
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_OP_PERMUTE, MOE_OP_GROUPED_MLP, MOE_OP_LAYER = 0, 1, 2
+(MOE_KERNEL_ROUTER, MOE_KERNEL_PERMUTE_SCATTER, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN,
+ MOE_KERNEL_COMBINE) = range(5)
 
 # every function the header declares
 EXPORTS = ("moe_status_string", "moe_check_config", "moe_capacity", "moe_max_kept",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_mlp", "moe_combine",
-           "moe_layer_forward")
+           "moe_layer_forward", "moe_time_next_launch")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -72,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_grouped_mlp": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_combine": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P]),
         "moe_layer_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "moe_time_next_launch": (ctypes.c_int, [ctypes.c_int, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -176,3 +180,9 @@ def moe_layer_forward(cfg, x, w_router, router_bias, w_gate, w_up, w_down, ws_ga
         ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward")
+
+
+def moe_time_next_launch(kernel: int, begin_event, end_event) -> None:
+    """Bracket the next launch of ``kernel`` on this thread with two hipEvent_t handles."""
+    _check(load_library().moe_time_next_launch(int(kernel), begin_event, end_event),
+           "moe_time_next_launch")

@@ -90,6 +90,12 @@ LayerWs layer_layout(const Shape& s, void* base) {
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 }  // namespace
+
+TimingRequest& timing_request() {
+  static thread_local TimingRequest r;
+  return r;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -223,6 +229,20 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   if (e == hipSuccess)
     e = launch_combine(s, w.y_perm, w.pos, w.gate, s.n_shared > 0 ? w.y_shared : nullptr, y, st);
   return hip_status(e);
+}
+
+moe_status moe_time_next_launch(int kernel, void* begin_event, void* end_event) {
+  TimingRequest& r = timing_request();
+  if (kernel == -1) {
+    r.kernel = -1;
+    return MOE_OK;
+  }
+  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_COMBINE || !begin_event || !end_event)
+    return MOE_ERR_INVALID_ARG;
+  r.kernel = kernel;
+  r.begin = static_cast<hipEvent_t>(begin_event);
+  r.end = static_cast<hipEvent_t>(end_event);
+  return MOE_OK;
 }
 
 }  // extern "C"

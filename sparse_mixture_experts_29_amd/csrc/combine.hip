@@ -87,6 +87,7 @@ hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos
   const int chunks = s.d / 8;
   const int tpb = chunks >= kThreads ? 1 : kThreads / chunks;
   const dim3 grid(static_cast<unsigned>((s.T + tpb - 1) / tpb));
+  timing_begin(MOE_KERNEL_COMBINE, st);
   if (s.dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(kThreads), 0, st,
                        static_cast<const bf16_t*>(y_perm), pos, gate,
@@ -97,6 +98,7 @@ hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos
                        static_cast<const float*>(y_perm), pos, gate,
                        static_cast<const float*>(y_shared), static_cast<float*>(y), s.T, s.d, s.k,
                        s.n_shared, tpb);
+  timing_end(MOE_KERNEL_COMBINE, st);
   return hipGetLastError();
 }
 

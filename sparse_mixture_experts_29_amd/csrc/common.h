@@ -61,6 +61,24 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
 hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos,
                           const float* gate, const void* y_shared, void* y, hipStream_t st);
 
+// Per-host-thread request of moe_time_next_launch.
+struct TimingRequest {
+  int kernel = -1;
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+TimingRequest& timing_request();
+inline void timing_begin(int kernel, hipStream_t st) {
+  TimingRequest& r = timing_request();
+  if (r.kernel == kernel) hipEventRecord(r.begin, st);
+}
+inline void timing_end(int kernel, hipStream_t st) {
+  TimingRequest& r = timing_request();
+  if (r.kernel == kernel) {
+    hipEventRecord(r.end, st);
+    r.kernel = -1;
+  }
+}
+
 inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace moe

@@ -21,178 +21,314 @@
 // one 8-byte write. LDS rows are 128 B; 16-byte chunk c of row r lives at chunk
 // c ^ (r & 7) ^ ((r >> 3) & 1), which keeps both the row-wise fills and the MFMA
 // operand reads (32 rows x one chunk) free of bank conflicts.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BM = 128;   // token rows per tile
-constexpr int BNW = 256;  // weight rows per tile
-constexpr int BK = 64;    // K per stage
+constexpr int BW = 256;          // weight rows per tile (gated: 128 gate + 128 up)
 constexpr int kTileEntries = 4;  // int32 per tile-table entry
+#ifndef MOE_GEMM_GROUP_M
+#define MOE_GEMM_GROUP_M 8
+#endif
+constexpr int kGroupM = MOE_GEMM_GROUP_M;  // m-tiles per raster group (L2 reuse of weight tiles)
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 32
+#endif
+#ifndef MOE_GEMM_NST
+#define MOE_GEMM_NST (MOE_GEMM_BK == 64 ? 2 : 4)
+#endif
+constexpr int BK = MOE_GEMM_BK;      // K per LDS stage
+constexpr int NST = MOE_GEMM_NST;    // LDS stages in the ring (stage = (256 + BT) * BK * 2 bytes)
+constexpr int CH = BK / 8;               // 16-byte chunks per LDS row
+constexpr int RPI = 64 / CH;             // LDS rows filled by one DMA instruction (1 KB)
+constexpr int IPW = 128 / RPI;           // DMA instructions per wave per stage (128 rows)
 
 struct GemmArgs {
-  const bf16_t* in_r;        // routed input rows: x [T][K] (gather) or h [rows][K]
-  const bf16_t* in_s;        // shared input rows: x [T][K] or hs [n_s*T][K]
+  const bf16_t* in_r;          // routed input rows: x [T][K] (gather) or h [rows][K]
+  const bf16_t* in_s;          // shared input rows: x [T][K] or hs [n_s*T][K]
   const int32_t* sorted_slot;  // gather for routed rows (gated launch), else nullptr
-  const int32_t* tiles;      // [n][4] {group, row_begin, row_end, 0}
-  const int32_t* n_tiles;    // device count
-  const bf16_t* w0_r;        // routed weights [E][N_r][K_r] (gate, or down)
-  const bf16_t* w1_r;        // routed up weights (gated)
-  const bf16_t* w0_s;        // shared weights [n_s][N_s][K_s]
+  const int32_t* tiles;        // [n][4] {group, row_begin, row_end, 0}
+  const int32_t* n_tiles;      // device count of m-tiles
+  const bf16_t* w0_r;          // routed weights [E][N_r][K_r] (gate, or down)
+  const bf16_t* w1_r;          // routed up weights (gated)
+  const bf16_t* w0_s;          // shared weights [n_s][N_s][K_s]
   const bf16_t* w1_s;
-  bf16_t* out_r;             // [rows][N_r]
-  bf16_t* out_s;             // [n_s*T][N_s]
+  bf16_t* out_r;               // [rows][N_r]
+  bf16_t* out_s;               // [n_s*T][N_s]
   int N_r, K_r, N_s, K_s;
   int E, k, T;
-  int m_bound;               // tile-table capacity (grid's m extent)
+  int n_tiles_n;               // n-tiles of the widest group
 };
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Chunk swizzle of LDS row r (its 16-byte chunk c is stored at slot c ^ swz(r)). It makes
+// 8 consecutive rows (32 banks) and 16 consecutive rows (64 banks) of one chunk column fall
+// in distinct bank groups, for the MFMA operand reads (32 rows, one chunk) and the DMA fills
+// (whole rows).
+__device__ __forceinline__ int swz(int r) {
+  return BK == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
+}
 
-template <bool GATED>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
-  const int m_idx = blockIdx.x % a.m_bound;
-  const int n_tile = blockIdx.x / a.m_bound;
-  if (m_idx >= *a.n_tiles) return;
-  const int g = a.tiles[m_idx * kTileEntries + 0];
-  const int row0 = a.tiles[m_idx * kTileEntries + 1];
-  const int row1 = a.tiles[m_idx * kTileEntries + 2];
-  const bool shared = g >= a.E;
-  const int N = shared ? a.N_s : a.N_r;
-  const int K = shared ? a.K_s : a.K_r;
-  constexpr int BNO = GATED ? BNW / 2 : BNW;  // output columns per tile
-  const int n0 = n_tile * BNO;
-  if (n0 >= N) return;
+typedef __attribute__((address_space(3))) void lds_void;
 
-  const int gi = shared ? g - a.E : g;
-  const bf16_t* w0 = (shared ? a.w0_s : a.w0_r) + static_cast<int64_t>(gi) * N * K;
-  const bf16_t* w1 = GATED ? (shared ? a.w1_s : a.w1_r) + static_cast<int64_t>(gi) * N * K : nullptr;
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maximum (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][(BNW + BM) * BK];
+// Workgroup barrier for the K loop. __syncthreads() would also wait for every outstanding
+// global access (vmcnt(0)), draining the DMA ring; here each wave has already waited for
+// the stage it needs with wait_vmcnt, so only the barrier itself is issued. The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int ch = tid & 7;   // 16-byte chunk within a 64-wide K row
-  const int rq = tid >> 3;  // 0..31: row within a group of 32
+// Global -> LDS fills of one stage (direct-to-LDS 16-byte loads, 1 KB per instruction).
+// LDS stage layout: rows 0..BW-1 weights, BW..BW+BT-1 tokens, BK*2 bytes per row.
+// Waves 0 and 1 each fill 128 weight rows, waves 2 and 3 each fill BT/2 token rows.
+// Instruction i of a wave fills its rows RPI*i .. RPI*i+RPI-1: lane l stores chunk slot
+// l%CH of row RPI*i + l/CH, i.e. the row's logical chunk (l%CH) ^ swz(row).
+// Offsets are 32-bit byte offsets from a wave-uniform base.
+struct DmaPlan {
+  const char* base;   // wave-uniform
+  uint32_t off[IPW];  // byte offset of this lane's chunk for instruction i (K offset 0)
 
-  // global row pointers for the fills (fixed over K)
-  const bf16_t* wp[BNW / 32];
+  template <int BT>
+  __device__ __forceinline__ void issue(bf16_t* stage, int k0, int wave) const {
+    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+    if (BT == 256 || wave < 2) {
+      bf16_t* dst = stage + wave * 128 * BK;
 #pragma unroll
-  for (int i = 0; i < BNW / 32; ++i) {
-    const int r = rq + 32 * i;
-    int n;
-    const bf16_t* base;
-    if (GATED) {
-      base = r < BNW / 2 ? w0 : w1;
-      n = n0 + (r < BNW / 2 ? r : r - BNW / 2);
+      for (int i = 0; i < IPW; ++i)
+        __builtin_amdgcn_global_load_lds(base + off[i] + kb, (lds_void*)(dst + i * RPI * BK), 16, 0, 0);
     } else {
-      base = w0;
-      n = n0 + r;
+      bf16_t* dst = stage + (BW + (wave - 2) * (BT / 2)) * BK;
+#pragma unroll
+      for (int i = 0; i < IPW * BT / 256; ++i)
+        __builtin_amdgcn_global_load_lds(base + off[i] + kb, (lds_void*)(dst + i * RPI * BK), 16, 0, 0);
     }
-    n = n < N ? n : N - 1;
-    wp[i] = base + static_cast<int64_t>(n) * K + ch * 8;
   }
-  const bf16_t* xp[BM / 32];
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    int row = row0 + rq + 32 * i;
-    row = row < row1 ? row : row0;
-    int64_t src;
-    if (shared) {
-      src = GATED ? row : static_cast<int64_t>(gi) * a.T + row;
-    } else {
-      src = GATED ? a.sorted_slot[row] / a.k : row;
-    }
-    xp[i] = (shared ? a.in_s : a.in_r) + src * K + ch * 8;
-  }
+};
 
-  u32x4 wreg[BNW / 32], xreg[BM / 32];
-  auto load_global = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < BNW / 32; ++i) wreg[i] = *reinterpret_cast<const u32x4*>(wp[i] + k0);
-#pragma unroll
-    for (int i = 0; i < BM / 32; ++i) xreg[i] = *reinterpret_cast<const u32x4*>(xp[i] + k0);
-  };
-  auto store_lds = [&](int st) {
-    bf16_t* wl = lds[st];
-    bf16_t* xl = lds[st] + BNW * BK;
-#pragma unroll
-    for (int i = 0; i < BNW / 32; ++i) {
-      const int r = rq + 32 * i;
-      *reinterpret_cast<u32x4*>(wl + r * BK + ((ch ^ swz(r)) << 3)) = wreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BM / 32; ++i) {
-      const int r = rq + 32 * i;
-      *reinterpret_cast<u32x4*>(xl + r * BK + ((ch ^ swz(r)) << 3)) = xreg[i];
-    }
-  };
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maximum (gfx9 encoding).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-  // wave tile: 128 weight rows (gated: 64 gate + 64 up) x 64 token rows
-  const int wn = wave & 1, wm = wave >> 1;
-  int wrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (GATED)
-      wrow[i] = (i < 2 ? 0 : BNW / 2) + wn * 64 + (i & 1) * 32;
+// wait until at most `later` stages of DMA (IPW instructions each) are still in flight
+__device__ __forceinline__ void wait_stages_in_flight(int later) {
+  if (later >= 3) wait_vmcnt<3 * IPW>();
+  else if (later == 2) wait_vmcnt<2 * IPW>();
+  else if (later == 1) wait_vmcnt<IPW>();
+  else wait_vmcnt<0>();
+}
+
+// Software-pipelined K loop of a full 256 x 256 tile (4 live token sub-tiles per wave),
+// BK = 32: every stage is 2 k-steps of 16 MFMAs. Issue order per stage, pinned with
+// scheduling barriers so the MFMA pipe never waits for a burst of memory instructions:
+//   A: 16 MFMAs of k-step 0, the first 8 each followed by one LDS read of k-step 1's
+//      operands, the next 4 each by one DMA instruction of stage kt+NST-1;
+//   B: 4 MFMAs of k-step 1, each followed by one more DMA instruction;
+//   -- wait for this wave's LDS reads and for stage kt+1's DMA, workgroup barrier --
+//   C: the last 12 MFMAs of k-step 1, the first 8 each followed by one LDS read of stage
+//      kt+1's k-step 0 operands (the last 4 cover the latency of those reads).
+// The barrier in the middle of the stage orders (i) every wave's reads of stage kt before
+// the DMA that reuses its slot, issued NST-1 stages later, and (ii) every wave's DMA of
+// stage kt+1 before the reads of C.
+__device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][4], bf16_t* lds,
+                                                const DmaPlan& dp, int K, int wave,
+                                                const int (&aoff)[4], const int (&boff)[4],
+                                                int swz_l, int khalf) {
+  constexpr int STAGE = (BW + 256) * BK;
+  const int KT = K / BK;
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto rd = [&](const bf16_t* st, int kk, int idx, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+    const int c = ((kk * 2 + khalf) ^ swz_l) << 3;
+    if (idx < 4)
+      fa[idx] = *reinterpret_cast<const bf16x8*>(st + aoff[idx] + c);
     else
-      wrow[i] = wn * 128 + i * 32;
-  }
-  const int xrow0 = wm * 64;
+      fb[idx - 4] = *reinterpret_cast<const bf16x8*>(st + boff[idx - 4] + c);
+  };
+  auto mf = [&](int m, const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+    const int i = m & 3, j = m >> 2;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  auto sb = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto dma = [&](bf16_t* dst, int i, uint32_t kb) {
+    __builtin_amdgcn_global_load_lds(dp.base + dp.off[i] + kb, (lds_void*)(dst + i * RPI * BK), 16, 0, 0);
+  };
 
-  f32x16 acc[4][2];
+  // prologue: stages 0..NST-2 in flight, wait for stage 0, fetch its k-step 0 operands
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < KT) dp.issue<256>(lds + s * STAGE, s * BK, wave);
+  wait_stages_in_flight(min(NST - 2, KT - 1));
+  stage_barrier();
+#pragma unroll
+  for (int r = 0; r < 8; ++r) rd(lds, 0, r, fa0, fb0);
+  sb();
+
+  // One stage of the pipeline. DMA: issue the fill of stage kt+NST-1 (steady state);
+  // NEXT: read stage kt+1's first operands after the barrier (every stage but the last).
+  // `later` = stages after kt+1 whose DMA may still be in flight at the barrier.
+  auto stage_step = [&](int kt, auto dma_on, auto next_on, int later) {
+    constexpr bool DMA = decltype(dma_on)::value;
+    constexpr bool NEXT = decltype(next_on)::value;
+    const bf16_t* cur = lds + (kt % NST) * STAGE;
+    const int nd = kt + NST - 1;
+    bf16_t* ddst = lds + (nd % NST) * STAGE + wave * 128 * BK;
+    const uint32_t kb = static_cast<uint32_t>(nd) * BK * 2u;
+    // A
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      mf(m, fa0, fb0);
+      sb();
+      if (m < 8) {
+        rd(cur, 1, m, fa1, fb1);
+        sb();
+      } else if (DMA && m < 12) {
+        dma(ddst, m - 8, kb);
+        sb();
+      }
+    }
+    // B
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      mf(m, fa1, fb1);
+      sb();
+      if (DMA) {
+        dma(ddst, 4 + m, kb);
+        sb();
+      }
+    }
+    if (NEXT) {
+      wait_lgkmcnt0();
+      wait_stages_in_flight(later);
+      stage_barrier();
+    }
+    // C
+    const bf16_t* nxt = lds + ((kt + 1) % NST) * STAGE;
+#pragma unroll
+    for (int m = 4; m < 16; ++m) {
+      mf(m, fa1, fb1);
+      sb();
+      if (NEXT && m < 12) {
+        rd(nxt, 0, m - 4, fa0, fb0);
+        sb();
+      }
+    }
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  // steady state: DMA every stage, NST-2 later stages in flight at each barrier
+  int kt = 0;
+  for (; kt + NST - 1 < KT; ++kt) stage_step(kt, yes{}, yes{}, NST - 2);
+  // drain: no more DMA; the last stage reads nothing after it
+  for (; kt + 1 < KT; ++kt) stage_step(kt, no{}, yes{}, KT - 2 - kt);
+  if (kt < KT) stage_step(kt, no{}, no{}, 0);
+}
+static_assert(IPW == 8 || BK != 32, "the pipelined loop issues 8 DMA instructions per stage");
+
+// K loop and epilogue of one wave, for LIVE (compile-time) token sub-tiles of 32 rows that
+// hold data. Every wave of a block runs the same number of K steps and barriers; waves
+// with fewer live sub-tiles skip MFMAs, not loads.
+template <bool GATED, int BT, int LIVE>
+__device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K, int wave,
+                                          int lane, int row0, int row1, int n0, int N,
+                                          bf16_t* out, int64_t out_row_base) {
+  constexpr int WT = BT / 2;
+  constexpr int STAGE = (BW + BT) * BK;  // bf16 elements per stage
+  const int wn = wave & 1, wm = wave >> 1;
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int tok0 = wm * WT;
+  const int swz_l = swz(l32);  // every row a lane reads is l32 + a multiple of 32
+  // LDS element offsets of this lane's operand rows
+  int aoff[4], boff[LIVE > 0 ? LIVE : 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    aoff[i] = ((GATED ? (i < 2 ? 0 : BW / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32) + l32) * BK;
+#pragma unroll
+  for (int j = 0; j < LIVE; ++j) boff[j] = (BW + tok0 + j * 32 + l32) * BK;
+
+  f32x16 acc[4][LIVE > 0 ? LIVE : 1];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < LIVE; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = K / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  const int l32 = lane & 31, khalf = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < KT) load_global((kt + 1) * BK);
-    const bf16_t* wl = lds[st];
-    const bf16_t* xl = lds[st] + BNW * BK;
+  constexpr int NB = LIVE > 0 ? LIVE : 1;
+  auto fetch = [&](const bf16_t* stage, int kk, bf16x8 (&af)[4], bf16x8 (&bf)[NB]) {
+    const int c = ((kk * 2 + khalf) ^ swz_l) << 3;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + khalf;
-      bf16x8 af[4], bfr[2];
+    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(stage + aoff[i] + c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wrow[i] + l32;
-        af[i] = *reinterpret_cast<const bf16x8*>(wl + r * BK + ((c ^ swz(r)) << 3));
-      }
+    for (int j = 0; j < LIVE; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(stage + boff[j] + c);
+  };
+  auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[NB]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = xrow0 + j * 32 + l32;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(xl + r * BK + ((c ^ swz(r)) << 3));
-      }
+    for (int j = 0; j < LIVE; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  };
+  // BK/16 k-steps of 16 per stage; operand fragments alternate between two register sets
+  // so the LDS reads of step kk+1 can be in flight while the MFMAs of step kk run
+  auto compute = [&](const bf16_t* stage) {
+    if (LIVE == 0) return;
+    bf16x8 a0[4], b0[NB], a1[4], b1[NB];
+    fetch(stage, 0, a0, b0);
+    fetch(stage, 1, a1, b1);
+    mma(a0, b0);
+    if (BK == 64) fetch(stage, 2, a0, b0);
+    mma(a1, b1);
+    if (BK == 64) {
+      fetch(stage, 3, a1, b1);
+      mma(a0, b0);
+      mma(a1, b1);
     }
-    if (kt + 1 < KT) store_lds(st ^ 1);
-    __syncthreads();
+  };
+  static_assert(BK == 64 || BK == 32, "compute() walks 2 or 4 k-steps of 16");
+
+  if constexpr (LIVE == 4 && BT == 256 && BK == 32 && NST >= 3) {
+    kloop_pipelined(acc, lds, dp, K, wave, aoff, boff, swz_l, khalf);
+  } else {
+    // Ring of NST LDS stages, DMA running NST-1 stages ahead of the MFMAs. At step kt the
+    // stage kt is complete once at most (NST-2) later stages of DMA are still in flight.
+    // (one back-edge and no early exit keeps the accumulators in place across iterations)
+    const int KT = K / BK;
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < KT) dp.issue<BT>(lds + s * STAGE, s * BK, wave);
+    for (int kt = 0; kt < KT; ++kt) {
+      // DMA instructions per stage: IPW, or IPW*BT/256 for token waves of a BT < 256 tile
+      if (kt + NST - 2 >= KT)
+        wait_vmcnt<0>();
+      else if (BT == 256 || wave < 2)
+        wait_vmcnt<(NST - 2) * IPW>();
+      else
+        wait_vmcnt<(NST - 2) * IPW * BT / 256>();
+      stage_barrier();
+      const int nxt = kt + NST - 1;
+      if (nxt < KT) dp.issue<BT>(lds + (nxt % NST) * STAGE, nxt * BK, wave);
+      compute(lds + (kt % NST) * STAGE);
+    }
   }
 
-  // epilogue. acc[i][j] register r of lane l: weight row wrow[i] + 8*(r/4) + 4*(l/32) + r%4,
-  // token row xrow0 + 32*j + l%32.
-  bf16_t* out = shared ? a.out_s : a.out_r;
+  // epilogue. acc[i][j] register r of lane l: weight row (operand A) 8*(r/4) + 4*(l/32) + r%4
+  // of sub-tile i, token row tok0 + 32*j + l%32.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = row0 + xrow0 + j * 32 + l32;
+  for (int j = 0; j < LIVE; ++j) {
+    const int row = row0 + tok0 + j * 32 + l32;
     if (row >= row1) continue;
-    const int64_t orow = shared ? static_cast<int64_t>(gi) * a.T + row : row;
-    bf16_t* op = out + orow * N;
+    bf16_t* op = out + (out_row_base + row) * N;
     if (GATED) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -218,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wrow[i] + q * 8 + khalf * 4;
+          const int n = n0 + wn * 128 + i * 32 + q * 8 + khalf * 4;
           if (n < N) {
             uint2 pk;
             pk.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
@@ -228,6 +364,101 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
         }
     }
   }
+}
+
+// One tile: BW weight rows x BT token rows, 4 waves as 2 (weights) x 2 (tokens), each
+// wave 128 weight rows x BT/2 tokens of v_mfma_f32_32x32x16_bf16 accumulators.
+template <bool GATED, int BT>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
+  constexpr int WT = BT / 2;  // token rows per wave
+  constexpr int TJ = WT / 32; // token sub-tiles per wave
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * (BW + BT) * BK];
+
+  // ---- XCD-aware, grouped block -> tile mapping (counts live on the device)
+  const int n_m = *a.n_tiles;
+  const int n_n = a.n_tiles_n;
+  const int G = n_m * n_n;
+#ifndef MOE_GEMM_NO_XCD
+  const int per_xcd = (G + 7) / 8;
+  const int slot = blockIdx.x / 8;
+  if (slot >= per_xcd) return;
+  const int L = (blockIdx.x % 8) * per_xcd + slot;
+#else
+  const int L = blockIdx.x;
+#endif
+  if (L >= G) return;
+  const int in_group = kGroupM * n_n;
+  const int first_m = (L / in_group) * kGroupM;
+  const int gsz = min(n_m - first_m, kGroupM);
+  const int m_idx = first_m + (L % in_group) % gsz;
+  const int n_tile = (L % in_group) / gsz;
+
+  // tile bookkeeping is wave-uniform: keep it in scalar registers
+  const int g = __builtin_amdgcn_readfirstlane(a.tiles[m_idx * kTileEntries + 0]);
+  const int row0 = __builtin_amdgcn_readfirstlane(a.tiles[m_idx * kTileEntries + 1]);
+  const int row1 = __builtin_amdgcn_readfirstlane(a.tiles[m_idx * kTileEntries + 2]);
+  const bool shared = g >= a.E;
+  const int N = shared ? a.N_s : a.N_r;
+  const int K = shared ? a.K_s : a.K_r;
+  constexpr int BNO = GATED ? BW / 2 : BW;  // output columns per tile
+  const int n0 = n_tile * BNO;
+  if (n0 >= N) return;
+  const int gi = shared ? g - a.E : g;
+  const bf16_t* w0 = (shared ? a.w0_s : a.w0_r) + static_cast<int64_t>(gi) * N * K;
+  const bf16_t* w1 = GATED ? (shared ? a.w1_s : a.w1_r) + static_cast<int64_t>(gi) * N * K : nullptr;
+  const bf16_t* in = shared ? a.in_s : a.in_r;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- DMA plan: waves 0-1 fill the weight rows, waves 2-3 the token rows. Rows past the
+  // end (weights past N, tokens past row1) re-read a valid row; their results are dropped.
+  DmaPlan dp;
+  const int lrow = lane / CH;  // row within an instruction's RPI rows
+  if (wave < 2) {
+    // gated: wave 0 the 128 gate rows, wave 1 the 128 up rows; else 128 rows each
+    const bf16_t* wb = GATED ? (wave == 0 ? w0 : w1) : w0;
+    const int nbase = GATED ? n0 : n0 + wave * 128;
+    dp.base = reinterpret_cast<const char*>(wb);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = i * RPI + lrow;  // row within the wave's 128 (row mod 128 fixes the swizzle)
+      const int n = min(nbase + r, N - 1);
+      const int c = (lane % CH) ^ swz(r);
+      dp.off[i] = static_cast<uint32_t>(n) * static_cast<uint32_t>(K) * 2u + (c << 4);
+    }
+  } else {
+    dp.base = reinterpret_cast<const char*>(in);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int tr = (wave - 2) * WT + i * RPI + lrow;  // token row within the tile
+      int r = row0 + tr;
+      r = r < row1 ? r : row0;
+      int64_t src;
+      if (shared)
+        src = GATED ? r : static_cast<int64_t>(gi) * a.T + r;
+      else
+        src = GATED ? a.sorted_slot[r] / a.k : r;
+      const int c = (lane % CH) ^ swz(BW + tr);
+      dp.off[i] = static_cast<uint32_t>(src * K * 2 + (c << 4));
+    }
+  }
+
+  bf16_t* out = shared ? a.out_s : a.out_r;
+  const int64_t out_row_base = shared ? static_cast<int64_t>(gi) * a.T : 0;
+  const int valid_rows = row1 - row0 - (wave >> 1) * WT;
+  const int live = __builtin_amdgcn_readfirstlane(valid_rows <= 0 ? 0 : min(TJ, (valid_rows + 31) / 32));
+  static_assert(TJ == 4 || TJ == 2, "token sub-tiles per wave");
+  if (live >= TJ)
+    tile_loop<GATED, BT, TJ>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+  else if (live == 0)
+    tile_loop<GATED, BT, 0>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+  else if (live == 1)
+    tile_loop<GATED, BT, 1>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+  else if (TJ == 4 && live == 2)
+    tile_loop<GATED, BT, (TJ == 4 ? 2 : 1)>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+  else
+    tile_loop<GATED, BT, (TJ == 4 ? 3 : 1)>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
 }
 
 // ---------------------------------------------------------------------------- fp32
@@ -370,7 +601,8 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   if (e == 0) *n_tiles = routed_tiles + n_shared * per_shared;
 }
 
-int tile_rows(const Shape& s) { return s.dtype == MOE_BF16 ? BM : FBM; }
+constexpr int kBT = 256;  // token rows per bf16 tile
+int tile_rows(const Shape& s) { return s.dtype == MOE_BF16 ? kBT : FBM; }
 
 int64_t m_tile_bound(const Shape& s) {
   const int bm = tile_rows(s);
@@ -426,7 +658,6 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.E = s.E;
     a.k = s.k;
     a.T = static_cast<int>(s.T);
-    a.m_bound = static_cast<int>(mb);
     // launch 1: h = silu(x Wg) * (x Wu)
     a.in_r = static_cast<const bf16_t*>(x);
     a.in_s = static_cast<const bf16_t*>(x);
@@ -440,9 +671,11 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.K_r = s.d;
     a.N_s = s.f_s;
     a.K_s = s.d;
-    const int64_t nt1 = (f_max + BNW / 2 - 1) / (BNW / 2);
-    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(static_cast<unsigned>(nt1 * mb)), dim3(kThreads),
-                       0, st, a);
+    a.n_tiles_n = static_cast<int>((f_max + BW / 2 - 1) / (BW / 2));
+    const int64_t g1 = (static_cast<int64_t>(a.n_tiles_n) * mb + 7) / 8 * 8;
+    timing_begin(MOE_KERNEL_GATE_UP, st);
+    hipLaunchKernelGGL((grouped_gemm_bf16<true, kBT>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0, st, a);
+    timing_end(MOE_KERNEL_GATE_UP, st);
     // launch 2: y = h Wd
     a.sorted_slot = nullptr;
     a.in_r = static_cast<const bf16_t*>(w.h);
@@ -457,9 +690,11 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.K_r = s.f;
     a.N_s = s.d;
     a.K_s = s.f_s;
-    const int64_t nt2 = (s.d + BNW - 1) / BNW;
-    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(static_cast<unsigned>(nt2 * mb)), dim3(kThreads),
-                       0, st, a);
+    a.n_tiles_n = (s.d + BW - 1) / BW;
+    const int64_t g2 = (static_cast<int64_t>(a.n_tiles_n) * mb + 7) / 8 * 8;
+    timing_begin(MOE_KERNEL_DOWN, st);
+    hipLaunchKernelGGL((grouped_gemm_bf16<false, kBT>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, st, a);
+    timing_end(MOE_KERNEL_DOWN, st);
   } else {
     GemmArgsF32 a{};
     a.sorted_slot = sorted_slot;
@@ -482,8 +717,10 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.N_s = s.f_s;
     a.K_s = s.d;
     const int64_t nt1 = (f_max + FBN - 1) / FBN;
+    timing_begin(MOE_KERNEL_GATE_UP, st);
     hipLaunchKernelGGL(grouped_gemm_f32<true>, dim3(static_cast<unsigned>(nt1 * mb)), dim3(256), 0,
                        st, a);
+    timing_end(MOE_KERNEL_GATE_UP, st);
     a.sorted_slot = nullptr;
     a.in_r = static_cast<const float*>(w.h);
     a.in_s = static_cast<const float*>(w.hs);
@@ -498,8 +735,10 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.N_s = s.d;
     a.K_s = s.f_s;
     const int64_t nt2 = (s.d + FBN - 1) / FBN;
+    timing_begin(MOE_KERNEL_DOWN, st);
     hipLaunchKernelGGL(grouped_gemm_f32<false>, dim3(static_cast<unsigned>(nt2 * mb)), dim3(256), 0,
                        st, a);
+    timing_end(MOE_KERNEL_DOWN, st);
   }
   return hipGetLastError();
 }

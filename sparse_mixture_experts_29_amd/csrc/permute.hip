@@ -183,9 +183,11 @@ hipError_t launch_permute(const Shape& s, const int32_t* idx, int32_t* counts, i
                      s.E, Epad, s.capacity, s.max_kept, counts, offsets, sorted_slot);
   int ebits = 0;
   while ((1 << ebits) < s.E) ++ebits;
+  timing_begin(MOE_KERNEL_PERMUTE_SCATTER, st);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(n_chunks), dim3(kThreads), 4 * s.E * sizeof(int),
                      st, idx, n_pairs, s.E, ebits, s.capacity, chunk_cnt, offsets, sorted_slot, pos,
                      drop);
+  timing_end(MOE_KERNEL_PERMUTE_SCATTER, st);
   return hipGetLastError();
 }
 

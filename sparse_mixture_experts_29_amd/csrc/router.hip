@@ -217,6 +217,7 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
   const int BT = small_e ? 64 : 16;
   const size_t lds = static_cast<size_t>(BT) * (s.E + 4) * sizeof(float);
   const dim3 grid((T + BT - 1) / BT), block(kRouterThreads);
+  timing_begin(MOE_KERNEL_ROUTER, st);
   if (s.dtype == MOE_BF16) {
     auto kern = small_e ? router_bf16_kernel<64> : router_bf16_kernel<16>;
     hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -232,6 +233,7 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
                        static_cast<const float*>(w_router), bias, idx, gate, logits, T, s.d, s.E,
                        s.k, s.gating);
   }
+  timing_end(MOE_KERNEL_ROUTER, st);
   return hipGetLastError();
 }
 
