@@ -109,7 +109,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="name of a configs.ALL entry")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before the timed steps, copy a buffer of this many MiB once (a plain copy "
+                         "kernel of known size, to scale the HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -141,6 +144,14 @@ def main():
     n_kept = int(b["offsets"][-1].item())
     touched = int((counts > 0).sum())
     del b
+
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ev = HipEvents()
     for _ in range(args.warmup):

@@ -129,33 +129,40 @@ __device__ __forceinline__ void wait_stages_in_flight(int later) {
   else wait_vmcnt<0>();
 }
 
-// Software-pipelined K loop of a full 256 x 256 tile (4 live token sub-tiles per wave),
-// BK = 32: every stage is 2 k-steps of 16 MFMAs. Issue order per stage, pinned with
-// scheduling barriers so the MFMA pipe never waits for a burst of memory instructions:
-//   A: 16 MFMAs of k-step 0, the first 8 each followed by one LDS read of k-step 1's
-//      operands, the next 4 each by one DMA instruction of stage kt+NST-1;
-//   B: 4 MFMAs of k-step 1, each followed by one more DMA instruction;
+// Software-pipelined K loop of a 256 x 256 tile in which this wave has LIVE (0..4) token
+// sub-tiles of 32 rows holding data; BK = 32, so every stage is 2 k-steps of NM = 4*LIVE
+// MFMAs. Issue order per stage, pinned with scheduling barriers so the MFMA pipe never
+// waits for a burst of memory instructions:
+//   A: the NM MFMAs of k-step 0, interleaved with the NR = 4 + LIVE LDS reads of k-step
+//      1's operands, then 4 DMA instructions of stage kt+NST-1;
+//   B: NM/4 MFMAs of k-step 1 with the other 4 DMA instructions;
 //   -- wait for this wave's LDS reads and for stage kt+1's DMA, workgroup barrier --
-//   C: the last 12 MFMAs of k-step 1, the first 8 each followed by one LDS read of stage
-//      kt+1's k-step 0 operands (the last 4 cover the latency of those reads).
+//   C: the remaining MFMAs of k-step 1, interleaved with the NR reads of stage kt+1's
+//      k-step 0 operands (the MFMAs after the last read cover its latency).
 // The barrier in the middle of the stage orders (i) every wave's reads of stage kt before
 // the DMA that reuses its slot, issued NST-1 stages later, and (ii) every wave's DMA of
-// stage kt+1 before the reads of C.
-__device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][4], bf16_t* lds,
+// stage kt+1 before the reads of C. All waves of a block pass the same number of
+// barriers (one per stage) whatever their LIVE, so waves of a ragged tile stay in step.
+template <int LIVE>
+__device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE : 1], bf16_t* lds,
                                                 const DmaPlan& dp, int K, int wave,
-                                                const int (&aoff)[4], const int (&boff)[4],
+                                                const int (&aoff)[4], const int (&boff)[LIVE > 0 ? LIVE : 1],
                                                 int swz_l, int khalf) {
   constexpr int STAGE = (BW + 256) * BK;
+  constexpr int NB = LIVE > 0 ? LIVE : 1;
+  constexpr int NM = 4 * LIVE;            // MFMAs per k-step
+  constexpr int NR = LIVE ? 4 + LIVE : 0; // LDS reads per k-step
+  constexpr int MB = NM / 4;              // MFMAs of k-step 1 before the barrier
   const int KT = K / BK;
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-  auto rd = [&](const bf16_t* st, int kk, int idx, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+  bf16x8 fa0[4], fb0[NB], fa1[4], fb1[NB];
+  auto rd = [&](const bf16_t* st, int kk, int idx, bf16x8 (&fa)[4], bf16x8 (&fb)[NB]) {
     const int c = ((kk * 2 + khalf) ^ swz_l) << 3;
     if (idx < 4)
       fa[idx] = *reinterpret_cast<const bf16x8*>(st + aoff[idx] + c);
     else
       fb[idx - 4] = *reinterpret_cast<const bf16x8*>(st + boff[idx - 4] + c);
   };
-  auto mf = [&](int m, const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+  auto mf = [&](int m, const bf16x8 (&fa)[4], const bf16x8 (&fb)[NB]) {
     const int i = m & 3, j = m >> 2;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
@@ -171,12 +178,12 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][4], bf16_t* lds
   wait_stages_in_flight(min(NST - 2, KT - 1));
   stage_barrier();
 #pragma unroll
-  for (int r = 0; r < 8; ++r) rd(lds, 0, r, fa0, fb0);
+  for (int r = 0; r < NR; ++r) rd(lds, 0, r, fa0, fb0);
   sb();
 
-  // One stage of the pipeline. DMA: issue the fill of stage kt+NST-1 (steady state);
-  // NEXT: read stage kt+1's first operands after the barrier (every stage but the last).
-  // `later` = stages after kt+1 whose DMA may still be in flight at the barrier.
+  // One stage. DMA: issue the fill of stage kt+NST-1 (steady state); NEXT: read stage
+  // kt+1's first operands after the barrier (every stage but the last). `later` = stages
+  // after kt+1 whose DMA may still be in flight at the barrier.
   auto stage_step = [&](int kt, auto dma_on, auto next_on, int later) {
     constexpr bool DMA = decltype(dma_on)::value;
     constexpr bool NEXT = decltype(next_on)::value;
@@ -185,23 +192,28 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][4], bf16_t* lds
     bf16_t* ddst = lds + (nd % NST) * STAGE + wave * 128 * BK;
     const uint32_t kb = static_cast<uint32_t>(nd) * BK * 2u;
     // A
+    constexpr int NA = NM > NR + 4 ? NM : NR + 4;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      mf(m, fa0, fb0);
-      sb();
-      if (m < 8) {
+    for (int m = 0; m < NA; ++m) {
+      if (m < NM) {
+        mf(m, fa0, fb0);
+        sb();
+      }
+      if (m < NR) {
         rd(cur, 1, m, fa1, fb1);
         sb();
-      } else if (DMA && m < 12) {
-        dma(ddst, m - 8, kb);
+      } else if (DMA && m < NR + 4) {
+        dma(ddst, m - NR, kb);
         sb();
       }
     }
     // B
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      mf(m, fa1, fb1);
-      sb();
+      if (m < MB) {
+        mf(m, fa1, fb1);
+        sb();
+      }
       if (DMA) {
         dma(ddst, 4 + m, kb);
         sb();
@@ -214,12 +226,15 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][4], bf16_t* lds
     }
     // C
     const bf16_t* nxt = lds + ((kt + 1) % NST) * STAGE;
+    constexpr int NC = NM - MB > NR ? NM - MB : NR;
 #pragma unroll
-    for (int m = 4; m < 16; ++m) {
-      mf(m, fa1, fb1);
-      sb();
-      if (NEXT && m < 12) {
-        rd(nxt, 0, m - 4, fa0, fb0);
+    for (int m = 0; m < NC; ++m) {
+      if (MB + m < NM) {
+        mf(MB + m, fa1, fb1);
+        sb();
+      }
+      if (NEXT && m < NR) {
+        rd(nxt, 0, m, fa0, fb0);
         sb();
       }
     }
@@ -297,8 +312,8 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
   };
   static_assert(BK == 64 || BK == 32, "compute() walks 2 or 4 k-steps of 16");
 
-  if constexpr (LIVE == 4 && BT == 256 && BK == 32 && NST >= 3) {
-    kloop_pipelined(acc, lds, dp, K, wave, aoff, boff, swz_l, khalf);
+  if constexpr (BT == 256 && BK == 32 && NST >= 3) {
+    kloop_pipelined<LIVE>(acc, lds, dp, K, wave, aoff, boff, swz_l, khalf);
   } else {
     // Ring of NST LDS stages, DMA running NST-1 stages ahead of the MFMAs. At step kt the
     // stage kt is complete once at most (NST-2) later stages of DMA are still in flight.
@@ -341,7 +356,7 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
             for (int u = 0; u < 4; ++u) {
               const float gv = acc[i][j][q * 4 + u];
               const float uv = acc[i + 2][j][q * 4 + u];
-              h[u] = gv / (1.0f + __expf(-gv)) * uv;
+              h[u] = silu_f32(gv) * uv;
             }
             uint2 pk;
             pk.x = pack_bf16x2(h[0], h[1]);
@@ -552,7 +567,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgsF32 a) {
       const int n = n0 + tx * 4 + j;
       if (n >= N) continue;
       float v = c0[i][j];
-      if (GATED) v = v / (1.0f + __expf(-v)) * c1[i][j];
+      if (GATED) v = silu_f32(v) * c1[i][j];
       out[orow * N + n] = v;
     }
   }

@@ -309,3 +309,19 @@ def test_planted_mistake_fails_a_pin(name, monkeypatch):
     monkeypatch.setattr(mo, fn_name, fn)
     monkeypatch.setattr(oracle, fn_name, fn, raising=False)
     assert not _run_pins_on_bruteforce(), f"mutant {name} survived the pins"
+
+
+@pytest.mark.parametrize("case", CASES[::5])
+def test_token_outputs_matches_bruteforce(case):
+    """The per-token form used at full sizes gives the brute force's outputs for any token
+    subset, given that token's routing and kept slots."""
+    seed, T, E, d, f, k, gating, cf, integer = case
+    x, wr, wg, wu, wd = _tiny_case(seed, T, E, d, f, integer)
+    r = _rng(9, seed)
+    sh = [(r.standard_normal((2, d)), r.standard_normal((2, d)), r.standard_normal((d, 2)))]
+    want = bf.layer(x.tolist(), wr.tolist(), None, wg.tolist(), wu.tolist(), wd.tolist(), k, gating, cf,
+                    [tuple(m.tolist() for m in s) for s in sh])
+    toks = np.arange(T)[::2]
+    got = oracle.token_outputs(x[toks], np.array(want["idx"])[toks], np.array(want["gate"])[toks],
+                               np.array(want["kept"])[toks], list(zip(wg, wu, wd)), sh, 1)
+    np.testing.assert_allclose(got, np.array(want["y"])[toks], rtol=1e-10, atol=1e-12)
