@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/moe.h"
 
 namespace moe {
@@ -53,6 +55,17 @@ size_t permute_ws_bytes(const Shape& s);
 // Grouped MLP: tile table + intermediate activations.
 size_t grouped_ws_bytes(const Shape& s);
 
+// Small batches (every group has at most kSmallMMaxRows rows): weight-streaming kernels.
+constexpr int kSmallMMaxRows = 64;
+bool use_small_m(const Shape& s);
+int small_m_splits(const Shape& s, bool gated);
+size_t small_m_ws_bytes(const Shape& s);
+hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t* sorted_slot,
+                                    const int32_t* offsets, const void* wg, const void* wu,
+                                    const void* wd, const void* swg, const void* swu,
+                                    const void* swd, void* h, void* hs, float* part,
+                                    void* y_perm, void* y_shared, hipStream_t st);
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_route(const Shape& s, const void* x, const void* w_router, const float* bias,
                         int32_t* idx, float* gate, float* logits, hipStream_t st);
@@ -74,12 +87,12 @@ struct TimingRequest {
 TimingRequest& timing_request();
 inline void timing_begin(int kernel, hipStream_t st) {
   TimingRequest& r = timing_request();
-  if (r.kernel == kernel) hipEventRecord(r.begin, st);
+  if (r.kernel == kernel) (void)hipEventRecord(r.begin, st);
 }
 inline void timing_end(int kernel, hipStream_t st) {
   TimingRequest& r = timing_request();
   if (r.kernel == kernel) {
-    hipEventRecord(r.end, st);
+    (void)hipEventRecord(r.end, st);
     r.kernel = -1;
   }
 }

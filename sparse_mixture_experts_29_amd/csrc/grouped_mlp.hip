@@ -629,6 +629,7 @@ struct GroupedWs {
   int32_t* n_tiles;
   void* h;
   void* hs;
+  float* part;  // small-batch path: split-K partials
 };
 
 GroupedWs carve(const Shape& s, void* ws) {
@@ -643,6 +644,8 @@ GroupedWs carve(const Shape& s, void* ws) {
   w.h = p;
   p += align256(static_cast<size_t>(s.max_kept) * s.f * es);
   w.hs = p;
+  p += align256(static_cast<size_t>(s.n_shared) * s.T * s.f_s * es);
+  w.part = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -652,7 +655,7 @@ size_t grouped_ws_bytes(const Shape& s) {
   const size_t es = s.dtype == MOE_BF16 ? 2 : 4;
   return align256(static_cast<size_t>(m_tile_bound(s)) * kTileEntries * sizeof(int32_t)) + 256 +
          align256(static_cast<size_t>(s.max_kept) * s.f * es) +
-         align256(static_cast<size_t>(s.n_shared) * s.T * s.f_s * es);
+         align256(static_cast<size_t>(s.n_shared) * s.T * s.f_s * es) + small_m_ws_bytes(s);
 }
 
 hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sorted_slot,
@@ -660,6 +663,9 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
                               const void* wd, const void* swg, const void* swu, const void* swd,
                               void* y_perm, void* y_shared, void* ws, hipStream_t st) {
   GroupedWs w = carve(s, ws);
+  if (use_small_m(s))
+    return launch_grouped_mlp_small(s, x, sorted_slot, offsets, wg, wu, wd, swg, swu, swd, w.h, w.hs,
+                                    w.part, y_perm, y_shared, st);
   const int bm = tile_rows(s);
   const int64_t mb = m_tile_bound(s);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, s.E, s.n_shared,

@@ -1,0 +1,413 @@
+// Grouped expert MLP for small batches (decode): every group holds at most 64 rows, so
+// the weights dominate the traffic and each weight element must be read from HBM once.
+// Pages: shubhamtatvamasi.com/llm-inference/moe, "Memory vs compute, quantified" and the Q&A
+// on batch size and decode (at small batches only the touched experts' weights are read,
+// and each step streams them from memory); klaylearn.com/glossary/mixture-of-experts
+// (decode gives tiny expert batches).
+//
+// One wave owns 16 weight rows (16 output columns) of one group and streams them straight
+// from HBM into the A operand of v_mfma_f32_16x16x32_bf16: lane l holds row l%16 and the 32
+// k values [32*(l/16), 32*(l/16)+32) of each 128-wide K block, as four 16-byte loads. The
+// token rows (operand B, one or two groups of 16 per wave) are read with the same K order,
+// so the MFMA sees a permuted K identical for both operands and the dot products are
+// unchanged. Operands (weights and token rows) are loaded two K blocks ahead through a ring of three
+// register sets.
+//   gated launch: h = silu(v Wg) * (v Wu) for 16 columns of f, all rows of the group; when
+//                 K is split, fp32 partials of both products, and a second kernel sums
+//                 them in split order and applies silu * mul;
+//   down launch:  split-K partial sums of h Wd in fp32, reduced in a fixed order by a
+//                 second kernel (deterministic, no atomics).
+// Work units = (token half, group, K split, 16-column chunk); units of empty groups exit at
+// once. K splits keep the units small, so the last, partly filled round of waves is short.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;  // 4 waves, one unit each
+
+struct SmallArgs {
+  const bf16_t* in_r;          // routed input rows: x [T][K] (gather) or h [max_kept][K]
+  const bf16_t* in_s;          // shared input rows: x [T][K] or hs [n_s*T][K]
+  const int32_t* sorted_slot;  // gated launch: routed rows gather x[sorted_slot[p] / k]
+  const int32_t* offsets;      // [E+1]
+  const bf16_t* w0_r;          // [E][N_r][K_r]
+  const bf16_t* w1_r;
+  const bf16_t* w0_s;          // [n_s][N_s][K_s]
+  const bf16_t* w1_s;
+  bf16_t* out_r;               // gated: h [max_kept][N_r]
+  bf16_t* out_s;               // gated: hs [n_s*T][N_s]
+  float* part;                 // K-split partials: gated [splits][rows][2][fw], down [splits][rows][N]
+  int N_r, K_r, N_s, K_s;
+  int E, k, T, n_shared;
+  int n_chunks;                // 16-column chunks of the widest group
+  int splits;                  // K splits; gated with 1 split writes h directly
+  int halves;                  // waves per (group, split, chunk), each NGW token groups
+  int fw;                      // gated partials: row stride is 2*fw (fw = widest N)
+  int64_t max_kept;
+};
+
+// K loop and epilogue of one unit with NG (compile-time) token groups of 16. Operands of
+// K block i+D-1 (weights and token rows) are loaded while block i is multiplied: a ring of
+// D register sets, so no load waits on the one before it.
+template <bool GATED, int NG, int D>
+__device__ __forceinline__ void small_m_unit(const SmallArgs& a, const bf16_t* w0, const bf16_t* w1,
+                                             const bf16_t* const (&xp)[2], int t0, int kbeg, int kend,
+                                             int quad, int l16, int M, int r0, int gi, bool shared,
+                                             int N, int n0, int split) {
+  struct Ops {
+    u32x4 wa[4], wb[4], xv[NG][4];
+  };
+  f32x4 acc0[NG], acc1[NG];
+#pragma unroll
+  for (int t = 0; t < NG; ++t) {
+    acc0[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // lane covers k in [ko, ko+32) of a 128-wide block at kb: ko = kb + 32*quad, 64 contiguous
+  // bytes per lane over the block's 4 loads, so every load touches both 128-byte lines of
+  // each row's 256 bytes. In the 64-wide tail (`full` false) quads 2-3 read k in [kb, kb+32)
+  // instead, which is in range, and the multiply zeroes what they read. Loads are issued
+  // unconditionally and left untouched until their block is multiplied, so the compiler's
+  // count of loads in flight stays exact and no wait drains the ring.
+  auto load = [&](Ops& o, int kb, bool full) {
+    const int ko = kb + (full || quad < 2 ? quad * 32 : 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      o.wa[c] = *reinterpret_cast<const u32x4*>(w0 + ko + c * 8);
+      if (GATED) o.wb[c] = *reinterpret_cast<const u32x4*>(w1 + ko + c * 8);
+#pragma unroll
+      for (int t = 0; t < NG; ++t) o.xv[t][c] = *reinterpret_cast<const u32x4*>(xp[t] + ko + c * 8);
+    }
+  };
+  // m: all ones, or zero for the dead lanes of the tail block
+  auto mma = [&](const Ops& o, unsigned m) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < NG; ++t) {
+        const bf16x8 x = __builtin_bit_cast(bf16x8, o.xv[t][c] & m);
+        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.wa[c] & m), x, acc0[t], 0, 0, 0);
+        if (GATED)
+          acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.wb[c] & m), x, acc1[t], 0, 0, 0);
+      }
+  };
+  auto mma_full = [&](const Ops& o) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < NG; ++t) {
+        const bf16x8 x = __builtin_bit_cast(bf16x8, o.xv[t][c]);
+        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.wa[c]), x, acc0[t], 0, 0, 0);
+        if (GATED)
+          acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.wb[c]), x, acc1[t], 0, 0, 0);
+      }
+  };
+  const int nfull = (kend - kbeg) / 128;        // full 128-wide blocks
+  const bool tail = (kend - kbeg) % 128 != 0;   // then a 64-wide block
+  const int nb = nfull + (tail ? 1 : 0);
+  auto load_block = [&](Ops& o, int b) { load(o, kbeg + b * 128, b < nfull); };
+  auto mma_block = [&](const Ops& o, int b) { mma(o, b < nfull || quad < 2 ? 0xFFFFFFFFu : 0u); };
+  // ring of D register sets: on entry to an iteration blocks i .. i+D-2 sit in o[0 .. D-2].
+  // The steady loop runs while every block it loads exists (no guards inside) and never
+  // multiplies the tail block; the peeled round after it finishes the last < 2D-1 blocks.
+  Ops o[D];
+  // unconditional (a unit of fewer than D-1 blocks reloads its last one): no branch ahead of
+  // the loop, so the wait counts inside it stay exact
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) load_block(o[j], min(j, nb - 1));
+  int i = 0;
+  for (; i + 2 * D - 1 <= nb; i += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      // issue block i+j+D-1 before multiplying block i+j; the scheduling barriers stop the
+      // compiler from hoisting the next block's multiplies above these loads
+      load_block(o[(j + D - 1) % D], i + j + D - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_full(o[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    if (i + j + D - 1 < nb) load_block(o[(j + D - 1) % D], i + j + D - 1);
+    if (i + j < nb) mma_block(o[j], i + j);
+  }
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j)
+    if (i + D + j < nb) mma_block(o[j], i + D + j);
+
+  // epilogue. 16x16 C layout: lane holds weight rows n0 + 4*quad + r (r = 0..3) for token
+  // column l16 of each group.
+  const int ncol = n0 + quad * 4;
+  if (ncol >= N) return;
+#pragma unroll
+  for (int t = 0; t < NG; ++t) {
+    const int tok = (t0 + t) * 16 + l16;
+    if (tok < M) {
+      const int row = r0 + tok;
+      if (GATED && a.splits > 1) {
+        const int64_t prow = shared ? a.max_kept + static_cast<int64_t>(gi) * a.T + row : row;
+        const int64_t rows_total = a.max_kept + static_cast<int64_t>(a.n_shared) * a.T;
+        float* pp = a.part + (static_cast<int64_t>(split) * rows_total + prow) * 2 * a.fw + ncol;
+        *reinterpret_cast<float4*>(pp) = make_float4(acc0[t][0], acc0[t][1], acc0[t][2], acc0[t][3]);
+        *reinterpret_cast<float4*>(pp + a.fw) = make_float4(acc1[t][0], acc1[t][1], acc1[t][2], acc1[t][3]);
+      } else if (GATED) {
+        const int64_t orow = shared ? static_cast<int64_t>(gi) * a.T + row : row;
+        bf16_t* op = (shared ? a.out_s : a.out_r) + orow * N + ncol;
+        uint2 pk;
+        pk.x = pack_bf16x2(silu_f32(acc0[t][0]) * acc1[t][0], silu_f32(acc0[t][1]) * acc1[t][1]);
+        pk.y = pack_bf16x2(silu_f32(acc0[t][2]) * acc1[t][2], silu_f32(acc0[t][3]) * acc1[t][3]);
+        *reinterpret_cast<uint2*>(op) = pk;
+      } else {
+        const int64_t prow = shared ? a.max_kept + static_cast<int64_t>(gi) * a.T + row : row;
+        const int64_t rows_total = a.max_kept + static_cast<int64_t>(a.n_shared) * a.T;
+        float* pp = a.part + (static_cast<int64_t>(split) * rows_total + prow) * N + ncol;
+        *reinterpret_cast<float4*>(pp) = make_float4(acc0[t][0], acc0[t][1], acc0[t][2], acc0[t][3]);
+      }
+    }
+  }
+}
+
+// NGW: token groups of 16 per wave (1 or 2, so the 3-deep ring fits the register file). A
+// group with more rows than NGW*16 is covered by `halves` passes, one per NGW token groups.
+// The half is the slowest unit index: in a typical small batch every group fits one half,
+// and the blocks of the other halves exit at once instead of idling inside working blocks.
+template <bool GATED, int NGW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void small_m_kernel(SmallArgs a) {
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (readfirstlane): everything derived from the unit stays in scalar registers
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // unit = (half, group, split, chunk) with the chunk fastest: the waves of a block share a
+  // group, so blocks of empty groups retire at once
+  const int G = a.E + a.n_shared;
+  const int nc = static_cast<int>(unit % a.n_chunks);
+  int64_t rest = unit / a.n_chunks;
+  const int split = static_cast<int>(rest % a.splits);
+  rest /= a.splits;
+  const int g = static_cast<int>(rest % G);
+  const int half = static_cast<int>(rest / G);
+  if (half >= a.halves) return;
+  const bool shared = g >= a.E;
+  const int gi = shared ? g - a.E : g;
+  int r0, M;
+  if (shared) {
+    r0 = 0;
+    M = a.T;
+  } else {
+    r0 = a.offsets[g];
+    M = a.offsets[g + 1] - r0;
+  }
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  M = __builtin_amdgcn_readfirstlane(M);
+  const int t0 = half * NGW;            // first token group of this wave
+  const int ng = ((M + 15) >> 4) - t0;  // token groups left for it
+  if (ng <= 0) return;
+  const int N = shared ? a.N_s : a.N_r;
+  const int K = shared ? a.K_s : a.K_r;
+  const int n0 = nc * 16;
+  if (n0 >= N) return;
+  const int ks = K / a.splits;  // multiple of 64 (host guarantees)
+  const int kbeg = split * ks, kend = kbeg + ks;
+
+  const int l16 = lane & 15, quad = lane >> 4;
+  const int n = min(n0 + l16, N - 1);
+  const bf16_t* w0 = (shared ? a.w0_s : a.w0_r) + (static_cast<int64_t>(gi) * N + n) * K;
+  const bf16_t* w1 = GATED ? (shared ? a.w1_s : a.w1_r) + (static_cast<int64_t>(gi) * N + n) * K : nullptr;
+  const bf16_t* in = shared ? a.in_s : a.in_r;
+
+  const bf16_t* xp[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = r0 + min((t0 + t) * 16 + l16, M - 1);
+    int64_t src;
+    if (shared)
+      src = GATED ? r : static_cast<int64_t>(gi) * a.T + r;
+    else
+      src = GATED ? a.sorted_slot[r] / a.k : r;
+    xp[t] = in + src * K;
+  }
+  if (NGW == 1 || ng <= 1)
+    small_m_unit<GATED, 1, 3>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split);
+  else
+    small_m_unit<GATED, 2, 3>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split);
+}
+
+// h = silu(sum of gate partials) * (sum of up partials), the sums over K splits in split
+// order, rounded once to bf16 (the gated epilogue of the K-split launch).
+__global__ __launch_bounds__(256) void small_m_swiglu_reduce(const float* __restrict__ part,
+                                                             const int32_t* __restrict__ offsets, int E,
+                                                             int64_t max_kept, int n_shared, int T, int f,
+                                                             int f_s, int fw, int splits,
+                                                             bf16_t* __restrict__ h,
+                                                             bf16_t* __restrict__ hs) {
+  const int64_t rows_total = max_kept + static_cast<int64_t>(n_shared) * T;
+  const int cq = fw / 4;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows_total * cq) return;
+  const int64_t row = i / cq;
+  const int c = static_cast<int>(i % cq) * 4;
+  const bool routed = row < max_kept;
+  if (routed ? (row >= offsets[E] || c >= f) : c >= f_s) return;
+  float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float* pp = part + (static_cast<int64_t>(sp) * rows_total + row) * 2 * fw + c;
+    const float4 vg = *reinterpret_cast<const float4*>(pp);
+    const float4 vu = *reinterpret_cast<const float4*>(pp + fw);
+    g.x += vg.x;
+    g.y += vg.y;
+    g.z += vg.z;
+    g.w += vg.w;
+    u.x += vu.x;
+    u.y += vu.y;
+    u.z += vu.z;
+    u.w += vu.w;
+  }
+  bf16_t* op = routed ? h + row * f + c : hs + (row - max_kept) * f_s + c;
+  uint2 pk;
+  pk.x = pack_bf16x2(silu_f32(g.x) * u.x, silu_f32(g.y) * u.y);
+  pk.y = pack_bf16x2(silu_f32(g.z) * u.z, silu_f32(g.w) * u.w);
+  *reinterpret_cast<uint2*>(op) = pk;
+}
+
+// y = sum over splits of the partials, in split order, rounded once to bf16.
+// One thread per 4 consecutive columns of one row; routed rows past N_kept are skipped.
+__global__ __launch_bounds__(256) void small_m_reduce(const float* __restrict__ part,
+                                                      const int32_t* __restrict__ offsets, int E,
+                                                      int64_t max_kept, int n_shared, int T, int N,
+                                                      int splits, bf16_t* __restrict__ y_perm,
+                                                      bf16_t* __restrict__ y_shared) {
+  const int64_t rows_total = max_kept + static_cast<int64_t>(n_shared) * T;
+  const int cq = N / 4;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows_total * cq) return;
+  const int64_t row = i / cq;
+  const int c = static_cast<int>(i % cq) * 4;
+  if (row < max_kept && row >= offsets[E]) return;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < splits; ++sp) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (static_cast<int64_t>(sp) * rows_total + row) * N + c);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  bf16_t* op = row < max_kept ? y_perm + row * N + c : y_shared + (row - max_kept) * N + c;
+  uint2 pk;
+  pk.x = pack_bf16x2(s.x, s.y);
+  pk.y = pack_bf16x2(s.z, s.w);
+  *reinterpret_cast<uint2*>(op) = pk;
+}
+
+int max_groups(const Shape& s) {
+  return static_cast<int>(std::min<int64_t>(s.E, s.T * s.k)) + s.n_shared;
+}
+
+}  // namespace
+
+bool use_small_m(const Shape& s) { return s.dtype == MOE_BF16 && s.T <= kSmallMMaxRows; }
+
+// K splits per launch: enough (group, chunk, split) units that the tail of the launch (the
+// last, partly filled round of waves) is short, while each split keeps >= 1024 of K.
+constexpr int64_t kSmallMUnitsTarget = 8192;
+
+int small_m_splits(const Shape& s, bool gated) {
+  const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
+  const int64_t units = static_cast<int64_t>(max_groups(s)) * ((gated ? fmax : s.d) / 16);
+  auto fits = [&](int sp) {  // every group's K splits into multiples of 64, each >= 1024
+    auto ok = [&](int K) { return K % sp == 0 && (K / sp) % 64 == 0 && K / sp >= 1024; };
+    if (gated) return ok(s.d);
+    return ok(s.f) && (s.n_shared == 0 || ok(s.f_s));
+  };
+  int sp = 1;
+  while (units * sp < kSmallMUnitsTarget && sp < 16 && fits(2 * sp)) sp *= 2;
+  return sp;
+}
+
+size_t small_m_ws_bytes(const Shape& s) {
+  if (!use_small_m(s)) return 0;
+  const int64_t rows_total = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
+  const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
+  const int sg = small_m_splits(s, true);
+  const size_t gated = sg > 1 ? static_cast<size_t>(sg) * rows_total * 2 * fmax * sizeof(float) : 0;
+  const size_t down = static_cast<size_t>(small_m_splits(s, false)) * rows_total * s.d * sizeof(float);
+  return align256(std::max(gated, down));
+}
+
+hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t* sorted_slot,
+                                    const int32_t* offsets, const void* wg, const void* wu,
+                                    const void* wd, const void* swg, const void* swu,
+                                    const void* swd, void* h, void* hs, float* part,
+                                    void* y_perm, void* y_shared, hipStream_t st) {
+  SmallArgs a{};
+  a.sorted_slot = sorted_slot;
+  a.offsets = offsets;
+  a.E = s.E;
+  a.k = s.k;
+  a.T = static_cast<int>(s.T);
+  a.n_shared = s.n_shared;
+  a.max_kept = s.max_kept;
+  const int G = s.E + s.n_shared;
+  // gated: h = silu(x Wg) * (x Wu)
+  a.in_r = static_cast<const bf16_t*>(x);
+  a.in_s = static_cast<const bf16_t*>(x);
+  a.w0_r = static_cast<const bf16_t*>(wg);
+  a.w1_r = static_cast<const bf16_t*>(wu);
+  a.w0_s = static_cast<const bf16_t*>(swg);
+  a.w1_s = static_cast<const bf16_t*>(swu);
+  a.out_r = static_cast<bf16_t*>(h);
+  a.out_s = static_cast<bf16_t*>(hs);
+  a.N_r = s.f;
+  a.K_r = s.d;
+  a.N_s = s.f_s;
+  a.K_s = s.d;
+  const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
+  a.n_chunks = fmax / 16;
+  a.splits = small_m_splits(s, true);
+  a.fw = fmax;
+  a.part = part;
+  int64_t units = static_cast<int64_t>(G) * a.n_chunks * a.splits;
+  // a group holds at most T rows (an expert appears once per token; the shared expert sees T)
+  const int groups16 = static_cast<int>((s.T + 15) / 16);
+  const int ngw = groups16 <= 1 ? 1 : 2;
+  a.halves = (groups16 + ngw - 1) / ngw;
+  auto kern_g = ngw == 1 ? small_m_kernel<true, 1> : small_m_kernel<true, 2>;
+  auto kern_d = ngw == 1 ? small_m_kernel<false, 1> : small_m_kernel<false, 2>;
+  units *= a.halves;
+  timing_begin(MOE_KERNEL_GATE_UP, st);
+  hipLaunchKernelGGL(kern_g, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(kThreads), 0, st, a);
+  timing_end(MOE_KERNEL_GATE_UP, st);
+  const int64_t rows_total = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
+  if (a.splits > 1) {
+    const int64_t threads = rows_total * (fmax / 4);
+    hipLaunchKernelGGL(small_m_swiglu_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st,
+                       part, offsets, s.E, s.max_kept, s.n_shared, static_cast<int>(s.T), s.f, s.f_s, fmax,
+                       a.splits, static_cast<bf16_t*>(h), static_cast<bf16_t*>(hs));
+  }
+  // down: split-K partials, then the ordered reduction
+  a.sorted_slot = nullptr;
+  a.in_r = static_cast<const bf16_t*>(h);
+  a.in_s = static_cast<const bf16_t*>(hs);
+  a.w0_r = static_cast<const bf16_t*>(wd);
+  a.w1_r = nullptr;
+  a.w0_s = static_cast<const bf16_t*>(swd);
+  a.w1_s = nullptr;
+  a.part = part;
+  a.N_r = s.d;
+  a.K_r = s.f;
+  a.N_s = s.d;
+  a.K_s = s.f_s;
+  a.n_chunks = s.d / 16;
+  a.splits = small_m_splits(s, false);
+  units = static_cast<int64_t>(G) * a.n_chunks * a.splits * a.halves;
+  timing_begin(MOE_KERNEL_DOWN, st);
+  hipLaunchKernelGGL(kern_d, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(kThreads), 0, st, a);
+  timing_end(MOE_KERNEL_DOWN, st);
+  const int64_t threads = rows_total * (s.d / 4);
+  hipLaunchKernelGGL(small_m_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st, part,
+                     offsets, s.E, s.max_kept, s.n_shared, static_cast<int>(s.T), s.d, a.splits,
+                     static_cast<bf16_t*>(y_perm), static_cast<bf16_t*>(y_shared));
+  return hipGetLastError();
+}
+
+}  // namespace moe

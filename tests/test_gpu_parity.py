@@ -28,6 +28,12 @@ CASES = [
     R(configs.DEEPSEEK_V3, T=200, d_model=256, d_ff=128, n_experts=300, top_k=8, n_shared=2,
       d_ff_shared=64),
     *[R(configs.mixtral_decode(t), d_model=512, d_ff=1024) for t in (1, 4, 16, 64)],
+    # small batches through the weight-streaming path, with a shared expert and a K tail
+    R(configs.DEEPSEEK_V3, T=40, d_model=320, d_ff=192, n_experts=64, d_ff_shared=320),
+    R(configs.QWEN3_FINE_CF, T=57, d_model=256, d_ff=128, n_experts=16, top_k=4),
+    # small batches wide enough to split K in both launches (a 64-wide tail inside each split)
+    R(configs.mixtral_decode(4), d_model=2176, d_ff=2176),
+    R(configs.DEEPSEEK_V3, T=8, d_model=2048, d_ff=2048, n_experts=16, top_k=4, d_ff_shared=2048),
 ]
 
 
@@ -126,3 +132,13 @@ def test_stream_argument_is_honoured():
         dev.forward(stream=s)
     s.synchronize()
     assert torch.equal(dev.y, ref)
+
+
+def test_small_batch_collapsed_router_fills_four_token_groups():
+    """64 tokens all routed to expert 5 first: one group of 64 rows (4 groups of 16)."""
+    cfg = R(configs.MIXTRAL_PREFILL, T=64, d_model=256, d_ff=512, n_experts=8, top_k=2)
+    li = make_inputs(cfg)
+    li.router_bias = np.zeros(8, np.float32)
+    li.router_bias[5] = 4.0
+    dev = DeviceLayer(li)
+    P.check_layer_full(li, dev)
