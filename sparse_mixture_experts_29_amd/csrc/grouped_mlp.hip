@@ -31,6 +31,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int BW = 256;          // weight rows per tile (gated: 128 gate + 128 up)
 constexpr int kTileEntries = 4;  // int32 per tile-table entry
+constexpr int kQueueInts = 16;   // tile counters of the persistent launches: 8 (one per XCD) each
 #ifndef MOE_GEMM_GROUP_M
 #define MOE_GEMM_GROUP_M 8
 #endif
@@ -62,6 +63,7 @@ struct GemmArgs {
   int N_r, K_r, N_s, K_s;
   int E, k, T;
   int n_tiles_n;               // n-tiles of the widest group
+  int32_t* queue;              // [8] per-XCD tile counters, zeroed by build_tiles_kernel
 };
 
 // Chunk swizzle of LDS row r (its 16-byte chunk c is stored at slot c ^ swz(r)). It makes
@@ -131,18 +133,20 @@ __device__ __forceinline__ void wait_stages_in_flight(int later) {
 
 // Software-pipelined K loop of a 256 x 256 tile in which this wave has LIVE (0..4) token
 // sub-tiles of 32 rows holding data; BK = 32, so every stage is 2 k-steps of NM = 4*LIVE
-// MFMAs. Issue order per stage, pinned with scheduling barriers so the MFMA pipe never
-// waits for a burst of memory instructions:
+// MFMAs. Issue order per stage, pinned with scheduling barriers:
 //   A: the NM MFMAs of k-step 0, interleaved with the NR = 4 + LIVE LDS reads of k-step
-//      1's operands, then 4 DMA instructions of stage kt+NST-1;
-//   B: NM/4 MFMAs of k-step 1 with the other 4 DMA instructions;
+//      1's operands and DMA instructions kDmaC.. of stage kt+NST-1, one every 4 MFMAs;
+//   B: NM/4 MFMAs of k-step 1 with the last DMA instruction;
 //   -- wait for this wave's LDS reads and for stage kt+1's DMA, workgroup barrier --
 //   C: the remaining MFMAs of k-step 1, interleaved with the NR reads of stage kt+1's
-//      k-step 0 operands (the MFMAs after the last read cover its latency).
-// The barrier in the middle of the stage orders (i) every wave's reads of stage kt before
-// the DMA that reuses its slot, issued NST-1 stages later, and (ii) every wave's DMA of
-// stage kt+1 before the reads of C. All waves of a block pass the same number of
-// barriers (one per stage) whatever their LIVE, so waves of a ragged tile stay in step.
+//      k-step 0 operands and the first kDmaC DMA instructions of stage kt+NST, whose slot
+//      (that of stage kt) every wave has finished reading at the barrier.
+// The 8 DMA instructions of a stage are thus spread over a whole stage's MFMAs: issued in
+// a burst they fill the load queue, and an in-order wave stuck behind a full queue stops
+// feeding the MFMA pipe. The barrier in the middle of the stage orders (i) every wave's
+// reads of stage kt before the DMA that reuses its slot, and (ii) every wave's DMA of stage
+// kt+1 before the reads of C. All waves of a block pass the same number of barriers (one
+// per stage) whatever their LIVE, so waves of a ragged tile stay in step.
 template <int LIVE>
 __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE : 1], bf16_t* lds,
                                                 const DmaPlan& dp, int K, int wave,
@@ -153,6 +157,7 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE
   constexpr int NM = 4 * LIVE;            // MFMAs per k-step
   constexpr int NR = LIVE ? 4 + LIVE : 0; // LDS reads per k-step
   constexpr int MB = NM / 4;              // MFMAs of k-step 1 before the barrier
+  constexpr int kDmaC = 3;                // DMA instructions of a stage issued a phase early
   const int KT = K / BK;
   bf16x8 fa0[4], fb0[NB], fa1[4], fb1[NB];
   auto rd = [&](const bf16_t* st, int kk, int idx, bf16x8 (&fa)[4], bf16x8 (&fb)[NB]) {
@@ -167,11 +172,15 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
   auto sb = [] { __builtin_amdgcn_sched_barrier(0); };
-  auto dma = [&](bf16_t* dst, int i, uint32_t kb) {
+  // DMA instruction i of stage `st` (its slot is st % NST)
+  auto dma = [&](int st, int i) {
+    bf16_t* dst = lds + (st % NST) * STAGE + wave * 128 * BK;
+    const uint32_t kb = static_cast<uint32_t>(st) * BK * 2u;
     __builtin_amdgcn_global_load_lds(dp.base + dp.off[i] + kb, (lds_void*)(dst + i * RPI * BK), 16, 0, 0);
   };
 
-  // prologue: stages 0..NST-2 in flight, wait for stage 0, fetch its k-step 0 operands
+  // prologue: stages 0..NST-2 in flight, wait for stage 0, fetch its k-step 0 operands,
+  // then the early part of stage NST-1 (its slot has never been used)
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < KT) dp.issue<256>(lds + s * STAGE, s * BK, wave);
@@ -179,20 +188,23 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE
   stage_barrier();
 #pragma unroll
   for (int r = 0; r < NR; ++r) rd(lds, 0, r, fa0, fb0);
+  if (NST - 1 < KT) {
+#pragma unroll
+    for (int i = 0; i < kDmaC; ++i) dma(NST - 1, i);
+  }
   sb();
 
-  // One stage. DMA: issue the fill of stage kt+NST-1 (steady state); NEXT: read stage
-  // kt+1's first operands after the barrier (every stage but the last). `later` = stages
-  // after kt+1 whose DMA may still be in flight at the barrier.
-  auto stage_step = [&](int kt, auto dma_on, auto next_on, int later) {
-    constexpr bool DMA = decltype(dma_on)::value;
+  // One stage. AB: issue the rest of stage kt+NST-1 in A and B; C: the early part of stage
+  // kt+NST in C; NEXT: read stage kt+1's first operands after the barrier (every stage but
+  // the last). `later` = stages after kt+1 whose DMA may still be in flight at the barrier.
+  auto stage_step = [&](int kt, auto ab_on, auto c_on, auto next_on, int later) {
+    constexpr bool AB = decltype(ab_on)::value;
+    constexpr bool DC = decltype(c_on)::value;
     constexpr bool NEXT = decltype(next_on)::value;
     const bf16_t* cur = lds + (kt % NST) * STAGE;
-    const int nd = kt + NST - 1;
-    bf16_t* ddst = lds + (nd % NST) * STAGE + wave * 128 * BK;
-    const uint32_t kb = static_cast<uint32_t>(nd) * BK * 2u;
-    // A
-    constexpr int NA = NM > NR + 4 ? NM : NR + 4;
+    // A: DMA instructions kDmaC .. kDmaC+3 after MFMAs 1, 5, 9, 13
+    constexpr int NA0 = NM > NR ? NM : NR;
+    constexpr int NA = NA0 > 14 ? NA0 : 14;
 #pragma unroll
     for (int m = 0; m < NA; ++m) {
       if (m < NM) {
@@ -202,20 +214,21 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE
       if (m < NR) {
         rd(cur, 1, m, fa1, fb1);
         sb();
-      } else if (DMA && m < NR + 4) {
-        dma(ddst, m - NR, kb);
+      }
+      if (AB && (m & 3) == 1 && (m >> 2) < 4) {
+        dma(kt + NST - 1, kDmaC + (m >> 2));
         sb();
       }
     }
-    // B
+    // B: the last DMA instruction after the second MFMA slot
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       if (m < MB) {
         mf(m, fa1, fb1);
         sb();
       }
-      if (DMA) {
-        dma(ddst, 4 + m, kb);
+      if (AB && m == 1 && kDmaC + 4 < IPW) {
+        dma(kt + NST - 1, kDmaC + 4);
         sb();
       }
     }
@@ -224,9 +237,10 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE
       wait_stages_in_flight(later);
       stage_barrier();
     }
-    // C
+    // C: DMA instructions 0 .. kDmaC-1 of stage kt+NST after MFMAs 2, 6, 10
     const bf16_t* nxt = lds + ((kt + 1) % NST) * STAGE;
-    constexpr int NC = NM - MB > NR ? NM - MB : NR;
+    constexpr int NC0 = NM - MB > NR ? NM - MB : NR;
+    constexpr int NC = NC0 > 4 * kDmaC - 1 ? NC0 : 4 * kDmaC - 1;
 #pragma unroll
     for (int m = 0; m < NC; ++m) {
       if (MB + m < NM) {
@@ -237,16 +251,26 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE
         rd(nxt, 0, m, fa0, fb0);
         sb();
       }
+      if (DC && (m & 3) == 2 && (m >> 2) < kDmaC) {
+        dma(kt + NST, m >> 2);
+        sb();
+      }
     }
   };
+  static_assert(kDmaC + 5 == IPW, "A issues 4 and B 1 of the DMA instructions after the first kDmaC");
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
-  // steady state: DMA every stage, NST-2 later stages in flight at each barrier
   int kt = 0;
-  for (; kt + NST - 1 < KT; ++kt) stage_step(kt, yes{}, yes{}, NST - 2);
+  // steady state: both DMA parts every stage, NST-2 later stages in flight at each barrier
+  for (; kt + NST < KT; ++kt) stage_step(kt, yes{}, yes{}, yes{}, NST - 2);
+  // the stage that issues the last stage's remaining DMA
+  if (kt + NST - 1 < KT) {
+    stage_step(kt, yes{}, no{}, yes{}, NST - 2);
+    ++kt;
+  }
   // drain: no more DMA; the last stage reads nothing after it
-  for (; kt + 1 < KT; ++kt) stage_step(kt, no{}, yes{}, KT - 2 - kt);
-  if (kt < KT) stage_step(kt, no{}, no{}, 0);
+  for (; kt + 1 < KT; ++kt) stage_step(kt, no{}, no{}, yes{}, KT - 2 - kt);
+  if (kt < KT) stage_step(kt, no{}, no{}, no{}, 0);
 }
 static_assert(IPW == 8 || BK != 32, "the pipelined loop issues 8 DMA instructions per stage");
 
@@ -382,26 +406,13 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
 }
 
 // One tile: BW weight rows x BT token rows, 4 waves as 2 (weights) x 2 (tokens), each
-// wave 128 weight rows x BT/2 tokens of v_mfma_f32_32x32x16_bf16 accumulators.
+// wave 128 weight rows x BT/2 tokens of v_mfma_f32_32x32x16_bf16 accumulators. L is the
+// tile's index in raster order: groups of kGroupM m-tiles sweep every n-tile, so a weight
+// tile is read by kGroupM m-tiles close together in time.
 template <bool GATED, int BT>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L, int n_m, int n_n) {
   constexpr int WT = BT / 2;  // token rows per wave
   constexpr int TJ = WT / 32; // token sub-tiles per wave
-  __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * (BW + BT) * BK];
-
-  // ---- XCD-aware, grouped block -> tile mapping (counts live on the device)
-  const int n_m = *a.n_tiles;
-  const int n_n = a.n_tiles_n;
-  const int G = n_m * n_n;
-#ifndef MOE_GEMM_NO_XCD
-  const int per_xcd = (G + 7) / 8;
-  const int slot = blockIdx.x / 8;
-  if (slot >= per_xcd) return;
-  const int L = (blockIdx.x % 8) * per_xcd + slot;
-#else
-  const int L = blockIdx.x;
-#endif
-  if (L >= G) return;
   const int in_group = kGroupM * n_n;
   const int first_m = (L / in_group) * kGroupM;
   const int gsz = min(n_m - first_m, kGroupM);
@@ -474,6 +485,45 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
     tile_loop<GATED, BT, (TJ == 4 ? 2 : 1)>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else
     tile_loop<GATED, BT, (TJ == 4 ? 3 : 1)>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+}
+
+// Persistent launch: one block per CU takes tiles from queues until all are done. The
+// tiles in raster order are cut into 8 contiguous ranges, one per XCD (each has its own
+// L2), and a block first drains the range of the XCD it runs on, then helps the others,
+// so the CUs finish together however unequal the tiles are (ragged tiles cost less).
+// Every block leaves once every counter is past its range.
+template <bool GATED, int BT>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
+  // one LDS object (a second one costs a full DMA drain per stage: the compiler's wait
+  // insertion then cannot tell the DMA targets from the operand reads); the tile index
+  // sits past the stage ring
+  constexpr int kRing = NST * (BW + BT) * BK;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[kRing + 64];
+  int* next_tile = reinterpret_cast<int*>(lds + kRing);
+  const int n_m = *a.n_tiles;
+  const int n_n = a.n_tiles_n;
+  const int G = n_m * n_n;
+  const int per_xcd = (G + 7) / 8;
+  // XCC_ID hardware register (bits 3:0): the XCD this block runs on
+  int xcd = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) & 15;
+  if (xcd >= 8) xcd = blockIdx.x & 7;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int L = -1;
+      for (int v = 0; v < 8 && L < 0; ++v) {
+        const int x = (xcd + v) & 7;
+        if (__hip_atomic_load(&a.queue[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= per_xcd) continue;
+        const int t = atomicAdd(&a.queue[x], 1);
+        if (t < per_xcd && x * per_xcd + t < G) L = x * per_xcd + t;
+      }
+      *next_tile = L;
+    }
+    __syncthreads();
+    const int L = __builtin_amdgcn_readfirstlane(*next_tile);
+    __syncthreads();  // every wave has read next_tile before it is written again
+    if (L < 0) return;
+    gemm_tile<GATED, BT>(a, lds, L, n_m, n_n);
+  }
 }
 
 // ---------------------------------------------------------------------------- fp32
@@ -578,9 +628,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgsF32 a) {
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int E, int n_shared, int T, int bm,
                                                            int32_t* __restrict__ tiles,
-                                                           int32_t* __restrict__ n_tiles) {
+                                                           int32_t* __restrict__ n_tiles,
+                                                           int32_t* __restrict__ queues) {
   __shared__ int scan[1024];
   const int e = threadIdx.x;
+  if (e < kQueueInts) queues[e] = 0;  // tile counters of the two persistent launches
   int rows = 0, base_row = 0;
   if (e < E) {
     base_row = offsets[e];
@@ -626,7 +678,7 @@ int64_t m_tile_bound(const Shape& s) {
 
 struct GroupedWs {
   int32_t* tiles;
-  int32_t* n_tiles;
+  int32_t* n_tiles;  // [0]: m-tile count; [16, 16 + kQueueInts): tile counters
   void* h;
   void* hs;
   float* part;  // small-batch path: split-K partials
@@ -658,6 +710,19 @@ size_t grouped_ws_bytes(const Shape& s) {
          align256(static_cast<size_t>(s.n_shared) * s.T * s.f_s * es) + small_m_ws_bytes(s);
 }
 
+// compute units of the current device (cached per device)
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sorted_slot,
                               const int32_t* offsets, const void* wg, const void* wu,
                               const void* wd, const void* swg, const void* swu, const void* swd,
@@ -668,8 +733,9 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
                                     w.part, y_perm, y_shared, st);
   const int bm = tile_rows(s);
   const int64_t mb = m_tile_bound(s);
+  int32_t* queues = w.n_tiles + 16;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, s.E, s.n_shared,
-                     static_cast<int>(s.T), bm, w.tiles, w.n_tiles);
+                     static_cast<int>(s.T), bm, w.tiles, w.n_tiles, queues);
   const int f_max = s.n_shared > 0 && s.f_s > s.f ? s.f_s : s.f;
   if (s.dtype == MOE_BF16) {
     GemmArgs a{};
@@ -693,7 +759,10 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.N_s = s.f_s;
     a.K_s = s.d;
     a.n_tiles_n = static_cast<int>((f_max + BW / 2 - 1) / (BW / 2));
-    const int64_t g1 = (static_cast<int64_t>(a.n_tiles_n) * mb + 7) / 8 * 8;
+    a.queue = queues;
+    // persistent: one block per CU (the LDS ring admits one), never more than the tiles
+    const int n_cu = cu_count();
+    const int64_t g1 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb);
     timing_begin(MOE_KERNEL_GATE_UP, st);
     hipLaunchKernelGGL((grouped_gemm_bf16<true, kBT>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0, st, a);
     timing_end(MOE_KERNEL_GATE_UP, st);
@@ -712,7 +781,8 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.N_s = s.d;
     a.K_s = s.f_s;
     a.n_tiles_n = (s.d + BW - 1) / BW;
-    const int64_t g2 = (static_cast<int64_t>(a.n_tiles_n) * mb + 7) / 8 * 8;
+    a.queue = queues + 8;
+    const int64_t g2 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb);
     timing_begin(MOE_KERNEL_DOWN, st);
     hipLaunchKernelGGL((grouped_gemm_bf16<false, kBT>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, st, a);
     timing_end(MOE_KERNEL_DOWN, st);
