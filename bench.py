@@ -16,7 +16,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -57,8 +56,8 @@ class HipEvents:
 
 
 def kernel_source_hash(name: str) -> str:
-    p = os.path.join(ROOT, "sparse_mixture_experts_29_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    from sparse_mixture_experts_29_amd.traffic_summary import source_hash
+    return source_hash(os.path.join(ROOT, "sparse_mixture_experts_29_amd", "csrc", name))
 
 
 def traffic_from_profile(kernel_file: str, workload: str):

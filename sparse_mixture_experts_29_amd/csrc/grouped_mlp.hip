@@ -12,15 +12,18 @@
 // tile, so expert sizes never travel to the host and a skewed expert simply owns more
 // tiles. Launch 1 (gated) computes h = silu(v Wg) * (v Wu) for a 128-column slice of f,
 // with the gate and up rows of that slice side by side in LDS; launch 2 computes
-// y = h Wd for a 256-column slice of d.
+// y = h Wd for a 256-column slice of d. (Batches of at most 64 tokens take the
+// weight-streaming kernels of grouped_mlp_small.hip instead.)
 //
-// bf16 tile: 256 threads (4 waves, 2 x 2), 256 weight rows x 128 token rows x BK 64,
-// two LDS stages (96 KB) filled from registers prefetched one K step ahead.
+// bf16 tile: 256 threads (4 waves, 2 x 2), 256 weight rows x 256 token rows, K in stages
+// of 32 held in a ring of 4 LDS stages (128 KB) filled by direct-to-LDS DMA
+// (global_load_lds, 16 bytes per lane) running two stages ahead of the MFMAs.
 // MFMA v_mfma_f32_32x32x16_bf16 with the WEIGHT rows as operand A and the token rows as
 // operand B: the accumulator then holds 4 consecutive output columns per lane, stored as
-// one 8-byte write. LDS rows are 128 B; 16-byte chunk c of row r lives at chunk
-// c ^ (r & 7) ^ ((r >> 3) & 1), which keeps both the row-wise fills and the MFMA
+// one 8-byte write. LDS rows are 64 B; 16-byte chunk c of row r lives at chunk
+// c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1), which keeps both the DMA fills and the MFMA
 // operand reads (32 rows x one chunk) free of bank conflicts.
+// The launch is persistent: one block per CU takes tiles from per-XCD queues.
 #include <type_traits>
 
 #include "common.h"

@@ -24,6 +24,17 @@ import statistics
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def source_hash(path: str) -> str:
+    """Hash of a source file's code: comments and blank lines do not count, so a record
+    stays valid across comment edits and goes stale on any change to the code."""
+    code = []
+    for line in open(path, encoding="utf-8"):
+        line = re.sub(r"//.*", "", line).rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
+
+
 def _rows(d):
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -71,7 +82,7 @@ def main():
     rec = summarize(a.fetch_dir, a.write_dir, a.copy_mib, a.kernel_regex)
     src = os.path.join(ROOT, "sparse_mixture_experts_29_amd", "csrc", a.source)
     rec["kernel"] = a.kernel_name
-    rec["source_sha256_16"] = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    rec["source_sha256_16"] = source_hash(src)
     rec["command"] = a.command
     out = os.path.join(ROOT, "profiles", "traffic_counters.json")
     d = json.load(open(out)) if os.path.exists(out) else {}
