@@ -61,14 +61,26 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     const int c = i % chunks;
     if (t >= n_tok) break;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int p = pos[t * k + j];
-      if (p < 0) continue;
-      const float g = gate[t * k + j];
-      float v[8];
-      Vec8<T>::load(y_perm + static_cast<int64_t>(p) * d + c * 8, v);
+    // slots in groups of 8: positions and gates first, then every row load of the group
+    // issued before any is used (a dropped slot reads row 0, which exists whenever T >= 1,
+    // and is discarded), then the sum in slot order, as if dropped slots were skipped
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      int pj[8];
+      float gj[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] = fmaf(g, v[u], acc[u]);
+      for (int q = 0; q < 8; ++q) {
+        const bool in = j0 + q < k;
+        pj[q] = in ? pos[t * k + j0 + q] : -1;
+        gj[q] = in ? gate[t * k + j0 + q] : 0.f;
+      }
+      float v[8][8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        Vec8<T>::load(y_perm + static_cast<int64_t>(pj[q] >= 0 ? pj[q] : 0) * d + c * 8, v[q]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = pj[q] >= 0 ? fmaf(gj[q], v[q][u], acc[u]) : acc[u];
     }
     for (int s = 0; s < n_shared; ++s) {
       float v[8];

@@ -9,61 +9,189 @@
 //      operand, token rows as B; fp32: plain FMA) and parked in LDS;
 //   2. each wave takes BT/4 tokens and runs k rounds of a wave-wide argmax over the
 //      token's E logits (key: larger logit, then lower index), then the gates.
-// The bf16 K loop reads 64 contiguous bytes per lane per operand: lane l covers
-// k in [32*(l/16), 32*(l/16)+32) of a 128-wide K block and feeds it to 4 MFMAs. The
-// MFMA sees a permuted K order, identical for both operands, so the dot products are
-// unchanged.
+// The bf16 K loop reads 32 contiguous bytes per lane per operand per 64-wide K block and
+// feeds them to 2 MFMAs; the MFMA sees a permuted K order, identical for both operands, so
+// the dot products are unchanged.
 #include "common.h"
 
 namespace moe {
 namespace {
 
 constexpr int kRouterThreads = 256;
-constexpr int kExpertChunk = 256;  // experts per MFMA pass (4 waves x 64)
+#ifndef MOE_ROUTER_BT
+#define MOE_ROUTER_BT 32
+#endif
+constexpr int kRouterBT = MOE_ROUTER_BT;  // tokens per block of the bf16 MFMA router
 
+// One step of a wave argmax (key: larger logit, then lower index) against the lane that
+// the DPP pattern CTRL selects within each row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ void dpp_argmax_step(float& v, int& e) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oe = __builtin_amdgcn_update_dpp(0, e, CTRL, 0xF, 0xF, false);
+  if (ov > v || (ov == v && oe < e)) {
+    v = ov;
+    e = oe;
+  }
+}
+
+// Wave argmax of (v, e), returned in every lane (wave-uniform). Within each row of 16 lanes:
+// DPP swaps with lane^1 and lane^2 (quad permutes), then the half-row and row mirrors, which
+// pair every lane with one across the halves already reduced; the four row winners (lanes
+// 0, 16, 32, 48) are then compared in scalar registers. DPP moves cost a VALU cycle, a
+// cross-lane shuffle through the LDS unit about a hundred.
+__device__ __forceinline__ void wave_argmax(float& v, int& e) {
+  dpp_argmax_step<0xB1>(v, e);   // quad_perm [1,0,3,2]: lane ^ 1
+  dpp_argmax_step<0x4E>(v, e);   // quad_perm [2,3,0,1]: lane ^ 2
+  dpp_argmax_step<0x141>(v, e);  // row_half_mirror: lane i <-> 7 - i in each 8
+  dpp_argmax_step<0x140>(v, e);  // row_mirror: lane i <-> 15 - i in each 16
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int be = __builtin_amdgcn_readlane(e, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    const int oe = __builtin_amdgcn_readlane(e, 16 * r);
+    if (ov > bv || (ov == bv && oe < be)) {
+      bv = ov;
+      be = oe;
+    }
+  }
+  v = bv;
+  e = be;
+}
+
+// Row (16-lane) versions of the argmax and of a sum: after the four DPP steps every lane of
+// a row holds the row's result.
+__device__ __forceinline__ void row_argmax(float& v, int& e) {
+  dpp_argmax_step<0xB1>(v, e);   // lane ^ 1
+  dpp_argmax_step<0x4E>(v, e);   // lane ^ 2
+  dpp_argmax_step<0x141>(v, e);  // half-row mirror
+  dpp_argmax_step<0x140>(v, e);  // row mirror
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_sum_step(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_sum(float v) {
+  v = dpp_sum_step<0xB1>(v);
+  v = dpp_sum_step<0x4E>(v);
+  v = dpp_sum_step<0x141>(v);
+  return dpp_sum_step<0x140>(v);
+}
+
+// Top-k and gates for E <= 256: each row of 16 lanes owns one token (a wave runs 4 tokens at
+// once) and lane li holds the candidates li, li+16, ... in registers; k rounds of row_argmax
+// pick the experts in descending order. Slot j is kept by lane j % 16 (k <= 32).
+template <int BT>
+__device__ void topk_rows(const float* lg, int ld, int t0, int T, int E, int k, int gating, int32_t* idx,
+                          float* gate) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, rq = lane >> 4;
+  constexpr int kTokPerWave = BT / 4;
+  constexpr int RMAX = 16;      // E <= 256
+  const int R = (E + 15) / 16;  // candidates per lane
+  for (int tt = 0; tt < kTokPerWave; tt += 4) {
+    const int tl = wave * kTokPerWave + tt + rq;
+    const int t = t0 + tl;
+    const bool live = tt + rq < kTokPerWave && t < T;
+    const float* row = lg + (live ? tl : 0) * ld;
+    float cand[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      const int e = li + 16 * r;
+      cand[r] = (r < R && e < E) ? row[e] : -INFINITY;
+    }
+    uint32_t taken = 0;  // bit r: candidate li + 16 r already chosen
+    float first = 0.f, my_l[2] = {0.f, 0.f};
+    int my_e[2] = {0, 0};
+    for (int j = 0; j < k; ++j) {
+      float bl = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) {
+        const int e = li + 16 * r;
+        const bool ok = r < R && e < E && !((taken >> r) & 1u);
+        const bool better = cand[r] > bl || (cand[r] == bl && e < be);
+        bl = ok && better ? cand[r] : bl;
+        be = ok && better ? e : be;
+      }
+      row_argmax(bl, be);
+      if ((be & 15) == li) taken |= 1u << (be >> 4);
+      if (li == (j & 15)) {
+        my_l[j >> 4] = bl;
+        my_e[j >> 4] = be;
+      }
+      if (j == 0) first = bl;
+    }
+    float p[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = li + 16 * h;
+      p[h] = j < k ? (gating == MOE_SOFTMAX ? __expf(my_l[h] - first) : sigmoid_f32(my_l[h])) : 0.f;
+    }
+    const float sum = row_sum(p[0] + p[1]);
+    if (live) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = li + 16 * h;
+        if (j < k) {
+          idx[static_cast<int64_t>(t) * k + j] = my_e[h];
+          gate[static_cast<int64_t>(t) * k + j] = p[h] / sum;
+        }
+      }
+    }
+  }
+}
+
+// Top-k and gates of the tokens of a block, from their logits in LDS (row tl at lg + tl*ld).
+// Each wave takes BT/4 tokens; lane l holds the candidates l, l+64, ... (E <= 1024) in
+// registers and k rounds of wave_argmax pick the experts in descending order.
 template <int BT>
 __device__ void topk_and_gates(const float* lg, int ld, int t0, int T, int E, int k, int gating,
                                int32_t* idx, float* gate) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kTokPerWave = BT / 4;
+  constexpr int RMAX = 16;      // E <= 1024
   const int R = (E + 63) / 64;  // candidates per lane
   for (int tt = 0; tt < kTokPerWave; ++tt) {
     const int tl = wave * kTokPerWave + tt;
     const int t = t0 + tl;
     if (t >= T) break;
     const float* row = lg + tl * ld;
+    float cand[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      const int e = lane + 64 * r;
+      cand[r] = (r < R && e < E) ? row[e] : -INFINITY;
+    }
     uint32_t taken = 0;  // bit r: candidate lane + 64 r already chosen
-    float chosen_l = 0.f;
-    int chosen_e = 0;
-    float my_l = 0.f;
+    float first = 0.f, my_l = 0.f;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
       // lane-local best among untaken candidates
       float bl = -INFINITY;
       int be = 0x7fffffff;
-      for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) {
         const int e = lane + 64 * r;
-        if (e < E && !((taken >> r) & 1u)) {
-          const float v = row[e];
-          if (v > bl || (v == bl && e < be)) { bl = v; be = e; }
+        if (r < R && e < E && !((taken >> r) & 1u) && (cand[r] > bl || (cand[r] == bl && e < be))) {
+          bl = cand[r];
+          be = e;
         }
       }
-      // wave argmax: larger logit, then lower index
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ol = __shfl_xor(bl, off);
-        const int oe = __shfl_xor(be, off);
-        if (ol > bl || (ol == bl && oe < be)) { bl = ol; be = oe; }
-      }
+      wave_argmax(bl, be);
       if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (lane == j) { my_l = bl; my_e = be; }
-      if (j == 0) { chosen_l = bl; chosen_e = be; }
+      if (lane == j) {
+        my_l = bl;
+        my_e = be;
+      }
+      if (j == 0) first = bl;
     }
-    (void)chosen_e;
     // gates over the k chosen logits held by lanes 0..k-1
     float p = 0.f;
-    if (lane < k) {
-      p = (gating == MOE_SOFTMAX) ? __expf(my_l - chosen_l) : sigmoid_f32(my_l);
-    }
+    if (lane < k) p = (gating == MOE_SOFTMAX) ? __expf(my_l - first) : sigmoid_f32(my_l);
     float sum = p;
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
     if (lane < k) {
@@ -71,6 +199,86 @@ __device__ void topk_and_gates(const float* lg, int ld, int t0, int T, int E, in
       gate[static_cast<int64_t>(t) * k + lane] = p / sum;
     }
   }
+}
+
+// One pass of the bf16 router for one wave: NJ expert tiles of 16 (tiles p0 + wave + 4j) x
+// NT token tiles of 16, logits (+ bias) parked in LDS. K is read in blocks of 64: lane
+// (row l16, quad) holds k in [kb + 16*quad, +16) as two 16-byte loads (the same permuted
+// order for both operands), through a ring of 3 register sets: block i+2 is loaded while
+// block i is multiplied. d is a multiple of 64, so there is no K tail.
+template <int NJ, int NT>
+__device__ __forceinline__ void router_pass(const bf16_t* __restrict__ w, const bf16_t* const (&xrow)[NT],
+                                            const float* __restrict__ bias, float* lg, int ld, int d, int E,
+                                            int p0, int wave, int quad, int l16) {
+  const int nkb = d / 64;
+  const bf16_t* wrow[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    int e = (p0 + wave + 4 * j) * 16 + l16;
+    e = e < E ? e : E - 1;
+    wrow[j] = w + static_cast<int64_t>(e) * d;
+  }
+  f32x4 acc[NJ][NT];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[j][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  struct Ops {
+    u32x4 a[NJ][2], b[NT][2];
+  };
+  auto load = [&](Ops& o, int blk) {
+    const int ko = blk * 64 + quad * 16;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) o.a[j][c] = *reinterpret_cast<const u32x4*>(wrow[j] + ko + c * 8);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o.b[nt][c] = *reinterpret_cast<const u32x4*>(xrow[nt] + ko + c * 8);
+    }
+  };
+  auto mma = [&](const Ops& o) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[j][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.a[j][c]),
+                                                               __builtin_bit_cast(bf16x8, o.b[nt][c]),
+                                                               acc[j][nt], 0, 0, 0);
+  };
+  constexpr int D = 3;
+  Ops o[D];
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) load(o[j], min(j, nkb - 1));
+  int i = 0;
+  for (; i + 2 * D - 1 <= nkb; i += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      load(o[(j + D - 1) % D], i + j + D - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(o[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    if (i + j + D - 1 < nkb) load(o[(j + D - 1) % D], i + j + D - 1);
+    if (i + j < nkb) mma(o[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j)
+    if (i + D + j < nkb) mma(o[j]);
+  // C layout (16x16): lane holds rows (experts) 4*quad + r of its tile, column (token) l16
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = (p0 + wave + 4 * j) * 16 + quad * 4 + r;
+        if (e < E) lg[(nt * 16 + l16) * ld + e] = acc[j][nt][r] + (bias ? bias[e] : 0.f);
+      }
 }
 
 template <int BT>
@@ -94,76 +302,20 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(
     xrow[nt] = x + static_cast<int64_t>(t) * d;
   }
 
-  for (int e0 = 0; e0 < E; e0 += kExpertChunk) {
-    const int ew = e0 + wave * 64;  // this wave's 64 experts
-    if (ew < E) {
-      const bf16_t* wrow[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        int e = ew + mt * 16 + l16;
-        e = e < E ? e : E - 1;
-        wrow[mt] = w + static_cast<int64_t>(e) * d;
-      }
-      f32x4 acc[4][NT];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-      int kb = 0;
-      for (; kb + 128 <= d; kb += 128) {
-        const int ko = kb + quad * 32;
-        u32x4 a[4][4], b[NT][4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) a[mt][c] = *reinterpret_cast<const u32x4*>(wrow[mt] + ko + c * 8);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) b[nt][c] = *reinterpret_cast<const u32x4*>(xrow[nt] + ko + c * 8);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, a[mt][c]), __builtin_bit_cast(bf16x8, b[nt][c]),
-                  acc[mt][nt], 0, 0, 0);
-      }
-      if (kb < d) {  // 64-wide tail: lane covers 16 k values
-        const int ko = kb + quad * 16;
-        u32x4 a[4][2], b[NT][2];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int c = 0; c < 2; ++c) a[mt][c] = *reinterpret_cast<const u32x4*>(wrow[mt] + ko + c * 8);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int c = 0; c < 2; ++c) b[nt][c] = *reinterpret_cast<const u32x4*>(xrow[nt] + ko + c * 8);
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, a[mt][c]), __builtin_bit_cast(bf16x8, b[nt][c]),
-                  acc[mt][nt], 0, 0, 0);
-      }
-      // C layout (16x16): lane holds rows (experts) 4*quad + i, column (token) l16
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = ew + mt * 16 + quad * 4 + i;
-            if (e < E) lg[(nt * 16 + l16) * ld + e] = acc[mt][nt][i] + (bias ? bias[e] : 0.f);
-          }
-    }
+  // Expert tiles of 16 go round-robin to the waves, at most 4 per wave per pass of 256
+  // experts, so all 4 waves work for any E >= 64; a wave runs the pass with exactly its
+  // number of live tiles (1..4).
+  const int n_et = (E + 15) / 16;
+  for (int p0 = 0; p0 < n_et; p0 += 16) {
+    const int nj = __builtin_amdgcn_readfirstlane(min(4, max(0, (n_et - p0 - wave + 3) / 4)));
+    if (nj == 4)
+      router_pass<4, NT>(w, xrow, bias, lg, ld, d, E, p0, wave, quad, l16);
+    else if (nj == 3)
+      router_pass<3, NT>(w, xrow, bias, lg, ld, d, E, p0, wave, quad, l16);
+    else if (nj == 2)
+      router_pass<2, NT>(w, xrow, bias, lg, ld, d, E, p0, wave, quad, l16);
+    else if (nj == 1)
+      router_pass<1, NT>(w, xrow, bias, lg, ld, d, E, p0, wave, quad, l16);
   }
   __syncthreads();
   if (logits) {
@@ -172,7 +324,10 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(
       if (t0 + tl < T) logits[static_cast<int64_t>(t0 + tl) * E + e] = lg[tl * ld + e];
     }
   }
-  topk_and_gates<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
+  if (E <= 256)
+    topk_rows<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
+  else
+    topk_and_gates<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
 }
 
 template <int BT>
@@ -206,7 +361,10 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
       if (t0 + tl < T) logits[static_cast<int64_t>(t0 + tl) * E + e] = lg[tl * ld + e];
     }
   }
-  topk_and_gates<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
+  if (E <= 256)
+    topk_rows<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
+  else
+    topk_and_gates<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
 }
 
 // Small expert counts (E <= 32): a block of 256 threads owns TB tokens and splits d over all
@@ -302,11 +460,7 @@ __global__ __launch_bounds__(256) void router_small_e_kernel(
   for (int j = 0; j < k; ++j) {
     float bl = (lane < E && !taken) ? my : -INFINITY;
     int be = (lane < E && !taken) ? lane : 0x7fffffff;
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ol = __shfl_xor(bl, off);
-      const int oe = __shfl_xor(be, off);
-      if (ol > bl || (ol == bl && oe < be)) { bl = ol; be = oe; }
-    }
+    wave_argmax(bl, be);
     if (lane == be) taken = true;
     if (lane == j) { mine_l = bl; mine_e = be; }
     if (j == 0) first = bl;
@@ -344,23 +498,27 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
     timing_end(MOE_KERNEL_ROUTER, st);
     return hipGetLastError();
   }
-  const bool small_e = s.E <= 256;
-  const int BT = small_e ? 64 : 16;
-  const size_t lds = static_cast<size_t>(BT) * (s.E + 4) * sizeof(float);
-  const dim3 grid((T + BT - 1) / BT), block(kRouterThreads);
+  const dim3 block(kRouterThreads);
   timing_begin(MOE_KERNEL_ROUTER, st);
   if (s.dtype == MOE_BF16) {
-    auto kern = small_e ? router_bf16_kernel<64> : router_bf16_kernel<16>;
+    // 32 tokens per block: twice the blocks of a 64-token tile, two waves per SIMD, and the
+    // logits tile of even E = 1024 fits LDS (32 x 1028 x 4 B)
+    constexpr int BT = kRouterBT;
+    const size_t lds = static_cast<size_t>(BT) * (s.E + 4) * sizeof(float);
+    auto kern = router_bf16_kernel<BT>;
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(lds));
-    hipLaunchKernelGGL(kern, grid, block, lds, st, static_cast<const bf16_t*>(x),
+    hipLaunchKernelGGL(kern, dim3((T + BT - 1) / BT), block, lds, st, static_cast<const bf16_t*>(x),
                        static_cast<const bf16_t*>(w_router), bias, idx, gate, logits, T, s.d, s.E,
                        s.k, s.gating);
   } else {
+    const bool small_e = s.E <= 256;
+    const int BT = small_e ? 64 : 16;
+    const size_t lds = static_cast<size_t>(BT) * (s.E + 4) * sizeof(float);
     auto kern = small_e ? router_f32_kernel<64> : router_f32_kernel<16>;
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(lds));
-    hipLaunchKernelGGL(kern, grid, block, lds, st, static_cast<const float*>(x),
+    hipLaunchKernelGGL(kern, dim3((T + BT - 1) / BT), block, lds, st, static_cast<const float*>(x),
                        static_cast<const float*>(w_router), bias, idx, gate, logits, T, s.d, s.E,
                        s.k, s.gating);
   }
