@@ -25,7 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+SMALL_BATCH_TOKENS = 64  # bf16 batches up to this size take the weight-streaming kernels
 METRIC = "routed tokens/sec per MoE layer; % of bf16 MFMA peak (prefill) / HBM peak (decode)"
 
 
@@ -177,8 +178,44 @@ def main():
 
     value = cfg.T * K / elapsed
     flops_gate_up = 4.0 * cfg.d_model * cfg.d_ff * n_kept + 4.0 * cfg.d_model * cfg.d_ff_shared * cfg.T * cfg.n_shared
-    achieved = flops_gate_up / (gate_up_ms.mean() * 1e-3) / 1e12
     layer_flops = (cfg.expert_flops_per_pair() * n_kept + cfg.shared_flops() + cfg.router_flops())
+    es = 2 if cfg.dtype == "bf16" else 4
+    small_batch = cfg.dtype == "bf16" and cfg.T <= SMALL_BATCH_TOKENS
+    if small_batch:
+        # weight-streaming path: HBM-bound; algorithmic bytes of the gated launch = the touched
+        # experts' gate and up weights (+ shared), the token rows read, the h rows written
+        bytes_gate_up = (2.0 * cfg.d_model * cfg.d_ff * es * touched
+                         + 2.0 * cfg.d_model * cfg.d_ff_shared * es * cfg.n_shared
+                         + cfg.T * cfg.d_model * es + n_kept * cfg.d_ff * es
+                         + cfg.n_shared * cfg.T * cfg.d_ff_shared * es)
+        achieved = bytes_gate_up / (gate_up_ms.mean() * 1e-3) / 1e9
+        roofline = {
+            "kernel": "small_m_kernel<gated> (weight-streaming gate/up + SiLU*mul)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profile("grouped_mlp_small.hip", cfg.name),
+            "avg_launch_ms": round(float(gate_up_ms.mean()), 4),
+            "bytes_per_launch": bytes_gate_up,
+        }
+    else:
+        achieved = flops_gate_up / (gate_up_ms.mean() * 1e-3) / 1e12
+        roofline = {
+            "kernel": "grouped_gemm_bf16<gated> (gate/up GEMM + SiLU*mul)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_from_profile("grouped_mlp.hip", cfg.name),
+            "avg_launch_ms": round(float(gate_up_ms.mean()), 4),
+            "flops_per_launch": flops_gate_up,
+        }
+    # whole-layer algorithmic bytes (weights of touched experts, router, x in and y out)
+    layer_bytes = (3.0 * cfg.d_model * cfg.d_ff * es * touched + 3.0 * cfg.d_model * cfg.d_ff_shared * es * cfg.n_shared
+                   + cfg.d_model * cfg.n_experts * es + 2.0 * cfg.T * cfg.d_model * es)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -196,23 +233,14 @@ def main():
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k, "gating": cfg.gating,
                    "capacity_factor": cfg.capacity_factor, "n_shared": cfg.n_shared,
                    "d_ff_shared": cfg.d_ff_shared, "parallelism": "single GPU"},
-        "roofline": {
-            "kernel": "grouped_gemm_bf16<gated> (gate/up GEMM + SiLU*mul)",
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic_from_profile("grouped_mlp.hip", cfg.name),
-            "avg_launch_ms": round(float(gate_up_ms.mean()), 4),
-            "flops_per_launch": flops_gate_up,
-        },
+        "roofline": roofline,
         "layer": {
             "step_ms_p50": round(float(np.percentile(step_ms, 50)), 4),
             "step_ms_p95": round(float(np.percentile(step_ms, 95)), 4),
             "step_ms_p99": round(float(np.percentile(step_ms, 99)), 4),
             "layer_tflops": round(layer_flops / (np.median(step_ms) * 1e-3) / 1e12, 2),
             "layer_mfma_frac": round(layer_flops / (np.median(step_ms) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "layer_hbm_frac": round(layer_bytes / (np.median(step_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "n_kept": n_kept,
             "experts_touched": touched,
             "max_over_mean_load": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),

@@ -223,6 +223,17 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   hipError_t e = launch_route(s, x, w_router, router_bias, w.idx, w.gate, nullptr, st);
   if (e == hipSuccess)
     e = launch_permute(s, w.idx, w.counts, w.offsets, w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
+  if (use_small_m(s)) {
+    // small batches: combine straight from the down launch's split-K partials (no y_perm
+    // round trip, one launch fewer; the same values as the staged calls)
+    if (e == hipSuccess)
+      e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, w_gate, w_up, w_down, ws_gate, ws_up,
+                             ws_down, nullptr, nullptr, w.grouped_ws, st);
+    if (e == hipSuccess)
+      e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false), w.pos,
+                                  w.gate, y, st);
+    return hip_status(e);
+  }
   if (e == hipSuccess)
     e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, w_gate, w_up, w_down, ws_gate, ws_up,
                            ws_down, w.y_perm, w.y_shared, w.grouped_ws, st);

@@ -92,7 +92,76 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   }
 }
 
+// Row chunk c of partial row `row`: the sum over the splits in split order, rounded to
+// bf16 and widened back (the value the ordered reduction stores into y_perm).
+__device__ __forceinline__ void split_sum_bf16(const float* __restrict__ part, int64_t row, int64_t rows_total,
+                                               int d, int c, int splits, float* v) {
+  float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float* pp = part + (static_cast<int64_t>(sp) * rows_total + row) * d + c * 8;
+    const float4 a = *reinterpret_cast<const float4*>(pp);
+    const float4 b = *reinterpret_cast<const float4*>(pp + 4);
+    s0.x += a.x;
+    s0.y += a.y;
+    s0.z += a.z;
+    s0.w += a.w;
+    s1.x += b.x;
+    s1.y += b.y;
+    s1.z += b.z;
+    s1.w += b.w;
+  }
+  const uint32_t w[4] = {pack_bf16x2(s0.x, s0.y), pack_bf16x2(s0.z, s0.w), pack_bf16x2(s1.x, s1.y),
+                         pack_bf16x2(s1.z, s1.w)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Small-batch layer: combine straight from the down launch's split-K partials (rows
+// [0, max_kept) routed, then max_kept + s*T + t for shared expert s), skipping the bf16
+// y_perm round trip; same arithmetic, same order as reduce + combine_kernel.
+__global__ __launch_bounds__(kThreads) void combine_partials_kernel(
+    const float* __restrict__ part, int splits, int64_t max_kept, const int32_t* __restrict__ pos,
+    const float* __restrict__ gate, bf16_t* __restrict__ y, int64_t n_tok, int d, int k, int n_shared) {
+  const int chunks = d / 8;
+  const int64_t rows_total = max_kept + static_cast<int64_t>(n_shared) * n_tok;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n_tok * chunks) return;
+  const int64_t t = i / chunks;
+  const int c = static_cast<int>(i % chunks);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int p = pos[t * k + j];
+    if (p < 0) continue;
+    const float g = gate[t * k + j];
+    float v[8];
+    split_sum_bf16(part, p, rows_total, d, c, splits, v);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = fmaf(g, v[u], acc[u]);
+  }
+  for (int s = 0; s < n_shared; ++s) {
+    float v[8];
+    split_sum_bf16(part, max_kept + static_cast<int64_t>(s) * n_tok + t, rows_total, d, c, splits, v);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += v[u];
+  }
+  Vec8<bf16_t>::store(y + t * d + c * 8, acc);
+}
+
 }  // namespace
+
+hipError_t launch_combine_partials(const Shape& s, const float* part, int splits, const int32_t* pos,
+                                   const float* gate, void* y, hipStream_t st) {
+  const int64_t threads = s.T * (s.d / 8);
+  timing_begin(MOE_KERNEL_COMBINE, st);
+  hipLaunchKernelGGL(combine_partials_kernel, dim3(static_cast<unsigned>((threads + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, part, splits, s.max_kept, pos, gate, static_cast<bf16_t*>(y), s.T,
+                     s.d, s.k, s.n_shared);
+  timing_end(MOE_KERNEL_COMBINE, st);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos,
                           const float* gate, const void* y_shared, void* y, hipStream_t st) {

@@ -60,11 +60,19 @@ constexpr int kSmallMMaxRows = 64;
 bool use_small_m(const Shape& s);
 int small_m_splits(const Shape& s, bool gated);
 size_t small_m_ws_bytes(const Shape& s);
+// y_perm == nullptr: stop after the down launch and leave the fp32 split-K partials in the
+// workspace (small_m_partials) for launch_combine_partials
 hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t* sorted_slot,
                                     const int32_t* offsets, const void* wg, const void* wu,
                                     const void* wd, const void* swg, const void* swu,
                                     const void* swd, void* h, void* hs, float* part,
                                     void* y_perm, void* y_shared, hipStream_t st);
+// the down launch's partials [splits][max_kept + n_s*T][d] inside the grouped-MLP workspace
+float* small_m_partials(const Shape& s, void* grouped_ws);
+// y from the partials: each kept slot's row is summed over the splits in order and rounded
+// to bf16 exactly as the reduction into y_perm does, then combined as launch_combine does
+hipError_t launch_combine_partials(const Shape& s, const float* part, int splits, const int32_t* pos,
+                                   const float* gate, void* y, hipStream_t st);
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_route(const Shape& s, const void* x, const void* w_router, const float* bias,

@@ -706,6 +706,8 @@ GroupedWs carve(const Shape& s, void* ws) {
 
 }  // namespace
 
+float* small_m_partials(const Shape& s, void* ws) { return carve(s, ws).part; }
+
 size_t grouped_ws_bytes(const Shape& s) {
   const size_t es = s.dtype == MOE_BF16 ? 2 : 4;
   return align256(static_cast<size_t>(m_tile_bound(s)) * kTileEntries * sizeof(int32_t)) + 256 +

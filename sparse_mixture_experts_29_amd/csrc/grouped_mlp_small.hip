@@ -310,6 +310,8 @@ bool use_small_m(const Shape& s) { return s.dtype == MOE_BF16 && s.T <= kSmallMM
 // K splits per launch: enough (group, chunk, split) units that the tail of the launch (the
 // last, partly filled round of waves) is short, while each split keeps >= 1024 of K.
 constexpr int64_t kSmallMUnitsTarget = 8192;
+// wave slots of one round: 256 CUs x 2 blocks of 4 waves (two waves per SIMD)
+constexpr int64_t kSmallMWaveSlots = 2048;
 
 int small_m_splits(const Shape& s, bool gated) {
   const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
@@ -320,6 +322,9 @@ int small_m_splits(const Shape& s, bool gated) {
     return ok(s.f) && (s.n_shared == 0 || ok(s.f_s));
   };
   int sp = 1;
+  // a gated launch whose units all fit one round (one or two experts: a single token) runs
+  // unsplit: no round tail to shorten, and no reduction launch
+  if (gated && units <= kSmallMWaveSlots) return 1;
   while (units * sp < kSmallMUnitsTarget && sp < 16 && fits(2 * sp)) sp *= 2;
   return sp;
 }
@@ -403,6 +408,7 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   timing_begin(MOE_KERNEL_DOWN, st);
   hipLaunchKernelGGL(kern_d, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(kThreads), 0, st, a);
   timing_end(MOE_KERNEL_DOWN, st);
+  if (y_perm == nullptr) return hipGetLastError();  // the caller combines from the partials
   const int64_t threads = rows_total * (s.d / 4);
   hipLaunchKernelGGL(small_m_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st, part,
                      offsets, s.E, s.max_kept, s.n_shared, static_cast<int>(s.T), s.d, a.splits,
