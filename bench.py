@@ -77,6 +77,112 @@ def traffic_from_profile(kernel_file: str, workload: str):
     return None
 
 
+def time_steps(step, K: int, warmup: int, stream):
+    """Warm up, then time exactly K calls of step() on `stream`, bracketing the gated launch
+    of each with HIP events (moe_time_next_launch). Returns (wall seconds, per-step ms,
+    per-step gated-launch ms)."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_29_amd import binding
+    ev = HipEvents()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    begins = [ev.create() for _ in range(K)]
+    ends = [ev.create() for _ in range(K)]
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_ev[0].record(stream)
+    for i in range(K):
+        binding.moe_time_next_launch(binding.MOE_KERNEL_GATE_UP, begins[i], ends[i])
+        step()
+        step_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(K)])
+    gate_up_ms = np.array([ev.elapsed_ms(begins[i], ends[i]) for i in range(K)])
+    for e in begins + ends:
+        ev.destroy(e)
+    return elapsed, step_ms, gate_up_ms
+
+
+def shard_bench(args, w):
+    """One GPU's share of an expert-parallel layer: route the whole layer on the GPU, keep
+    the rows whose experts this shard owns, and time moe_expert_shard_forward on them."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_29_amd import binding
+    from sparse_mixture_experts_29_amd.device import ExpertShard, host_to_device, shard_rows
+    from sparse_mixture_experts_29_amd.inputs import make_inputs
+
+    cfg = w.layer
+    binding.load_library()
+    li = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    x = host_to_device(li.x, cfg, dev)
+    wr = host_to_device(li.w_router, cfg, dev)
+    bias = None if li.router_bias is None else torch.from_numpy(li.router_bias).to(dev)
+    idx = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev)
+    gate = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev)
+    binding.moe_route(cfg, x, wr, bias, idx, gate, None)
+    tok, slot, local = shard_rows(idx.cpu().numpy(), w.n_shards, w.shard, cfg.n_experts)
+    del wr, idx, gate
+    sh = ExpertShard.from_inputs(li, w.n_shards, w.shard, x, tok, local, threads=16)
+    torch.cuda.synchronize()
+    R = len(tok)
+    per = cfg.n_experts // w.n_shards
+    loads = np.bincount(local, minlength=per)
+    elapsed, step_ms, gate_up_ms = time_steps(sh.forward, args.steps, args.warmup, torch.cuda.current_stream())
+    K = args.steps
+    es = 2 if cfg.dtype == "bf16" else 4
+    flops_gate_up = 4.0 * cfg.d_model * cfg.d_ff * R
+    if cfg.dtype == "bf16" and R <= SMALL_BATCH_TOKENS:
+        touched = int((loads > 0).sum())
+        bytes_gate_up = 2.0 * cfg.d_model * cfg.d_ff * es * touched + R * cfg.d_model * es + R * cfg.d_ff * es
+        achieved = bytes_gate_up / (gate_up_ms.mean() * 1e-3) / 1e9
+        roofline = {"kernel": "small_m_kernel<gated> (weight-streaming gate/up + SiLU*mul)", "bound": "hbm",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "avg_launch_ms": round(float(gate_up_ms.mean()), 4), "bytes_per_launch": bytes_gate_up}
+    else:
+        achieved = flops_gate_up / (gate_up_ms.mean() * 1e-3) / 1e12
+        roofline = {"kernel": "grouped_gemm_bf16<gated> (gate/up GEMM + SiLU*mul)", "bound": "mfma",
+                    "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "avg_launch_ms": round(float(gate_up_ms.mean()), 4), "flops_per_launch": flops_gate_up}
+    shard_flops = cfg.expert_flops_per_pair() * R
+    out = {
+        "metric": "received rows/sec of one expert-parallel shard (moe_expert_shard_forward)",
+        "value": round(R * K / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) random-init weights)",
+        "config": {"workload": w.name, "layer": cfg.name, "n_shards": w.n_shards, "shard": w.shard,
+                   "rows": R, "local_experts": per, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
+                   "parallelism": "one GPU's expert shard (the exchanges are not run)"},
+        "roofline": roofline,
+        "layer": {
+            "step_ms_p50": round(float(np.percentile(step_ms, 50)), 4),
+            "step_ms_p95": round(float(np.percentile(step_ms, 95)), 4),
+            "step_ms_p99": round(float(np.percentile(step_ms, 99)), 4),
+            "shard_tflops": round(shard_flops / (np.median(step_ms) * 1e-3) / 1e12, 2),
+            "max_over_mean_load": round(float(loads.max() / max(loads.mean(), 1e-9)), 3),
+            "experts_touched": int((loads > 0).sum()),
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(li, n_tokens: int):
     """The oracle (as it stands) on the first n_tokens of the workload, on host cores."""
     import numpy as np
@@ -107,7 +213,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None, help="name of a configs.ALL entry")
+    ap.add_argument("--workload", default=None, help="name of a configs.ALL or configs.SHARDS entry")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -126,6 +232,8 @@ def main():
     from sparse_mixture_experts_29_amd.device import DeviceLayer
     from sparse_mixture_experts_29_amd.inputs import make_inputs
 
+    if args.workload in configs.SHARDS:
+        return shard_bench(args, configs.SHARDS[args.workload])
     cfg = configs.ALL[args.workload] if args.workload else configs.MIXTRAL_PREFILL
     binding.load_library()
     li = make_inputs(cfg)
@@ -153,29 +261,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ev = HipEvents()
-    for _ in range(args.warmup):
-        dev.forward()
-    torch.cuda.synchronize()
-
+    elapsed, step_ms, gate_up_ms = time_steps(dev.forward, args.steps, args.warmup, stream)
     K = args.steps
-    begins = [ev.create() for _ in range(K)]
-    ends = [ev.create() for _ in range(K)]
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    step_ev[0].record(stream)
-    for i in range(K):
-        binding.moe_time_next_launch(binding.MOE_KERNEL_GATE_UP, begins[i], ends[i])
-        dev.forward()
-        step_ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(K)])
-    gate_up_ms = np.array([ev.elapsed_ms(begins[i], ends[i]) for i in range(K)])
-    for e in begins + ends:
-        ev.destroy(e)
-
     value = cfg.T * K / elapsed
     flops_gate_up = 4.0 * cfg.d_model * cfg.d_ff * n_kept + 4.0 * cfg.d_model * cfg.d_ff_shared * cfg.T * cfg.n_shared
     layer_flops = (cfg.expert_flops_per_pair() * n_kept + cfg.shared_flops() + cfg.router_flops())

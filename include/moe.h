@@ -161,6 +161,28 @@ MOE_API moe_status moe_layer_forward(const moe_config* cfg, const void* x, const
                              const void* ws_down, void* y, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* Expert-parallel shard (pages: shubhamtatvamasi.com/llm-inference/moe, section on serving
+ * MoE across GPUs: each GPU holds a subset of the experts, token rows are dispatched to the
+ * GPU that owns their expert and the expert outputs are sent back to be combined at home;
+ * klaylearn "Mixture of Experts" definition: permute by destination expert, grouped GEMM,
+ * undo the permutation). The part of one layer step that runs on the GPU owning
+ * E_local = cfg->n_experts experts, for the R = cfg->T rows it received:
+ *   y_send[r] = (silu(x_recv[r] . Wg_e) * (x_recv[r] . Wu_e)) . Wd_e,  e = local_expert[r]
+ * cfg: top_k must be 1, capacity_factor <= 0 (any capacity is applied where the rows are
+ * dispatched) and n_shared 0 (shared experts run at home with the home tokens).
+ * x_recv [R][d], local_expert [R] int32, y_send [R][d]; w_gate/w_up/w_down hold the local
+ * experts only, laid out as for moe_grouped_mlp. Rows keep their order, so the rows received
+ * from each source stay one contiguous slice of y_send for the return exchange. A row whose
+ * local_expert is outside [0, E_local) is treated as dropped: its y_send row is 0.
+ * Each output row is the same computation, in the same order, as that row's y_perm entry
+ * in a one-GPU layer whose grouped MLP takes the same kernel path (batches of at most 64
+ * rows take the weight-streaming kernels, larger ones the tiled GEMM).
+ * Needs ws of MOE_OP_LAYER bytes for cfg. */
+MOE_API moe_status moe_expert_shard_forward(const moe_config* cfg, const void* x_recv,
+                                    const int32_t* local_expert, const void* w_gate,
+                                    const void* w_up, const void* w_down, void* y_send, void* ws,
+                                    size_t ws_bytes, void* stream);
+
 /* Instrumentation, for measuring one kernel inside a layer call. The next launch of
  * `kernel` (MOE_KERNEL_*) made by any entry point called on THIS host thread is bracketed
  * by hipEventRecord(begin_event) and hipEventRecord(end_event) on that call's stream;

@@ -28,7 +28,7 @@ MOE_OP_PERMUTE, MOE_OP_GROUPED_MLP, MOE_OP_LAYER = 0, 1, 2
 # every function the header declares
 EXPORTS = ("moe_status_string", "moe_check_config", "moe_capacity", "moe_max_kept",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_mlp", "moe_combine",
-           "moe_layer_forward", "moe_time_next_launch")
+           "moe_layer_forward", "moe_expert_shard_forward", "moe_time_next_launch")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -75,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_grouped_mlp": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_combine": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P]),
         "moe_layer_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "moe_expert_shard_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_time_next_launch": (ctypes.c_int, [ctypes.c_int, _P, _P]),
     }
     for name, (res, args) in sig.items():
@@ -180,6 +181,12 @@ def moe_layer_forward(cfg, x, w_router, router_bias, w_gate, w_up, w_down, ws_ga
         ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward")
+
+
+def moe_expert_shard_forward(cfg, x_recv, local_expert, w_gate, w_up, w_down, y_send, ws, stream=None):
+    _check(load_library().moe_expert_shard_forward(
+        ctypes.byref(_cfg(cfg)), _ptr(x_recv), _ptr(local_expert), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(y_send), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_expert_shard_forward")
 
 
 def moe_time_next_launch(kernel: int, begin_event, end_event) -> None:

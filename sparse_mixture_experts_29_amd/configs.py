@@ -99,6 +99,24 @@ ALL = {c.name: c for c in [TINY_FP32, MIXTRAL_PREFILL, *[mixtral_decode(t) for t
                            QWEN3_FINE, QWEN3_FINE_CF, DEEPSEEK_V3]}
 
 
+@dataclasses.dataclass(frozen=True)
+class ShardWorkload:
+    """One GPU's share of an expert-parallel layer: `layer` routed over all its experts
+    (global T tokens), the GPU owning experts [shard*E/n, (shard+1)*E/n) runs the rows routed
+    there (moe_expert_shard_forward)."""
+    name: str
+    layer: LayerConfig
+    n_shards: int
+    shard: int
+
+
+SHARDS = {w.name: w for w in [
+    ShardWorkload("deepseek_v3_ep8_shard0_T16384_d7168_f2048_E256_k8", DEEPSEEK_V3, 8, 0),
+    ShardWorkload("qwen3_fine_ep8_shard0_T8192_d2048_f768_E128_k8", QWEN3_FINE, 8, 0),
+    ShardWorkload("mixtral_prefill_ep8_shard0_T4096_d4096_f14336_E8_k2", MIXTRAL_PREFILL, 8, 0),
+]}
+
+
 def reduced(cfg: LayerConfig, **kw) -> LayerConfig:
     """Same structure (gating, skew recipe, shared experts, capacity) at a smaller size."""
     name = cfg.name.split("_T")[0] + "_reduced_" + "_".join(f"{k}{v}" for k, v in sorted(kw.items()))

@@ -242,6 +242,37 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   return hip_status(e);
 }
 
+moe_status moe_expert_shard_forward(const moe_config* cfg, const void* x_recv, const int32_t* local_expert,
+                                    const void* w_gate, const void* w_up, const void* w_down, void* y_send,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status r = to_shape(cfg, &s);
+  if (r != MOE_OK) return r;
+  if (s.k != 1 || s.capacity >= 0 || s.n_shared != 0) return MOE_ERR_INVALID_ARG;
+  if (s.T == 0) return MOE_OK;
+  if (!x_recv || !local_expert || !w_gate || !w_up || !w_down || !y_send || !ws) return MOE_ERR_INVALID_ARG;
+  LayerWs w = layer_layout(s, ws);
+  if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the rows' expert ids are the top-1 choice of a router that ran elsewhere: permute them,
+  // run the grouped MLP, and gather each row's output back into receive order (unit gates)
+  hipError_t e = launch_permute(s, local_expert, w.counts, w.offsets, w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
+  if (use_small_m(s)) {
+    if (e == hipSuccess)
+      e = launch_grouped_mlp(s, x_recv, w.sorted_slot, w.offsets, w_gate, w_up, w_down, nullptr, nullptr,
+                             nullptr, nullptr, nullptr, w.grouped_ws, st);
+    if (e == hipSuccess)
+      e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false), w.pos,
+                                  nullptr, y_send, st);
+    return hip_status(e);
+  }
+  if (e == hipSuccess)
+    e = launch_grouped_mlp(s, x_recv, w.sorted_slot, w.offsets, w_gate, w_up, w_down, nullptr, nullptr, nullptr,
+                           w.y_perm, nullptr, w.grouped_ws, st);
+  if (e == hipSuccess) e = launch_combine(s, w.y_perm, w.pos, nullptr, nullptr, y_send, st);
+  return hip_status(e);
+}
+
 moe_status moe_time_next_launch(int kernel, void* begin_event, void* end_event) {
   TimingRequest& r = timing_request();
   if (kernel == -1) {

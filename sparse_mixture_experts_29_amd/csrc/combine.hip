@@ -5,6 +5,7 @@
 // imbalance" (a dropped pair skips its expert: it contributes nothing here);
 // klaylearn.com/glossary/mixture-of-experts, definition ("undoing the permutation").
 //
+// gate == nullptr means unit gates (the expert-parallel shard returns each row's output).
 // A gather, not a scatter: each block owns tokens and reads their k rows of y_perm, so
 // the fp32 sum runs in a fixed order (j ascending, then shared experts) and is
 // bit-reproducible. Each thread handles 8 consecutive elements (16 B of bf16).
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
       for (int q = 0; q < 8; ++q) {
         const bool in = j0 + q < k;
         pj[q] = in ? pos[t * k + j0 + q] : -1;
-        gj[q] = in ? gate[t * k + j0 + q] : 0.f;
+        gj[q] = in ? (gate ? gate[t * k + j0 + q] : 1.f) : 0.f;
       }
       float v[8][8];
 #pragma unroll
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void combine_partials_kernel(
   for (int j = 0; j < k; ++j) {
     const int p = pos[t * k + j];
     if (p < 0) continue;
-    const float g = gate[t * k + j];
+    const float g = gate ? gate[t * k + j] : 1.f;
     float v[8];
     split_sum_bf16(part, p, rows_total, d, c, splits, v);
 #pragma unroll

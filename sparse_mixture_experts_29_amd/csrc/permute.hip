@@ -7,6 +7,8 @@
 //
 // Pair s = t*k + j. Each token picks an expert at most once, so ascending s within an
 // expert is ascending token order, and "keep the lowest tokens" is "keep rank < C".
+// An expert id outside [0, E) (possible only in rows handed to moe_expert_shard_forward)
+// marks its pair dropped; it is never used as an index.
 // Three launches (one, permute_single_kernel, when the pairs fit one chunk), all
 // deterministic (no order-dependent atomics):
 //   1. hist:    per chunk of 1024 pairs, a per-expert count (LDS counters).
@@ -32,7 +34,10 @@ __global__ __launch_bounds__(kThreads) void permute_hist_kernel(const int32_t* _
   const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kPermuteChunk;
   for (int i = threadIdx.x; i < kPermuteChunk; i += kThreads) {
     const int64_t s = s0 + i;
-    if (s < n_pairs) atomicAdd(&cnt[idx[s]], 1);
+    if (s < n_pairs) {
+      const int e = idx[s];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&cnt[e], 1);
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kThreads)
@@ -154,6 +159,13 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
   for (int r = 0; r < kPairsPerThread; ++r) {
     const int64_t s = s_wave + r * 64 + lane;
     ex[r] = s < n_pairs ? idx[s] : -1;
+    if (static_cast<unsigned>(ex[r]) >= static_cast<unsigned>(E)) {
+      if (s < n_pairs) {  // an expert id outside [0, E): the pair is dropped
+        pos[s] = -1;
+        drop[s] = 1;
+      }
+      ex[r] = -1;
+    }
     if (ex[r] >= 0) atomicAdd(&wbase[wave * E + ex[r]], 1);
   }
   __syncthreads();
@@ -190,6 +202,13 @@ __global__ __launch_bounds__(kThreads) void permute_single_kernel(
   for (int r = 0; r < kPairsPerThread; ++r) {
     const int64_t s = s_wave + r * 64 + lane;
     ex[r] = s < n_pairs ? idx[s] : -1;
+    if (static_cast<unsigned>(ex[r]) >= static_cast<unsigned>(E)) {
+      if (s < n_pairs) {  // an expert id outside [0, E): the pair is dropped
+        pos[s] = -1;
+        drop[s] = 1;
+      }
+      ex[r] = -1;
+    }
     if (ex[r] >= 0) atomicAdd(&wbase[wave * E + ex[r]], 1);
   }
   __syncthreads();

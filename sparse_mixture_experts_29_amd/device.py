@@ -125,3 +125,68 @@ class DeviceLayer:
 
     def combine(self, b: dict, stream=None):
         binding.moe_combine(self.cfg, b["y_perm"], b["pos"], b["gate"], b["y_shared"], b["y"], stream)
+
+
+def shard_rows(idx, n_shards: int, shard: int, n_experts: int):
+    """The rows the GPU owning shard `shard` of an expert-parallel layer receives: every
+    (token, slot) pair whose expert lies in that shard's contiguous range of E / n_shards
+    experts, in source order (home GPUs own contiguous token ranges), then token, then slot.
+    Returns (token, slot, local expert id) arrays."""
+    per = n_experts // n_shards
+    idx = np.asarray(idx)
+    tok, slot = np.nonzero(idx // per == shard)  # row-major: ascending token, then slot
+    return tok, slot, (idx[tok, slot] - shard * per).astype(np.int32)
+
+
+class ExpertShard:
+    """One shard of an expert-parallel layer on this GPU: the received rows, their local
+    expert ids and the shard's expert weights; forward() runs moe_expert_shard_forward.
+    Build it from a DeviceLayer (views of its weights) or from seeded inputs (only the
+    shard's experts are generated and uploaded)."""
+
+    def __init__(self, cfg: LayerConfig, n_shards: int, shard: int, x, w_gate, w_up, w_down, tok, local_expert):
+        per = cfg.n_experts // n_shards
+        dev = x.device
+        self.tok = torch.as_tensor(tok, dtype=torch.int64, device=dev)
+        self.local_expert = torch.as_tensor(local_expert, dtype=torch.int32, device=dev)
+        R = int(self.tok.numel())
+        self.cfg = cfg.replace(name=f"{cfg.name}_shard{shard}of{n_shards}", T=R, n_experts=per, top_k=1,
+                               capacity_factor=0.0, n_shared=0, d_ff_shared=0)
+        self.x_recv = x.index_select(0, self.tok).contiguous()
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        self.y_send = torch.empty_like(self.x_recv)
+        self.ws = torch.empty(max(binding.moe_workspace_size(self.cfg, binding.MOE_OP_LAYER), 1), dtype=torch.uint8,
+                              device=dev)
+
+    @classmethod
+    def from_layer(cls, layer: DeviceLayer, n_shards: int, shard: int, tok, local_expert) -> "ExpertShard":
+        per = layer.cfg.n_experts // n_shards
+        e0 = shard * per
+        return cls(layer.cfg, n_shards, shard, layer.x, layer.w_gate[e0:e0 + per], layer.w_up[e0:e0 + per],
+                   layer.w_down[e0:e0 + per], tok, local_expert)
+
+    @classmethod
+    def from_inputs(cls, li: LayerInputs, n_shards: int, shard: int, x, tok, local_expert, threads: int = 8):
+        cfg = li.cfg
+        per = cfg.n_experts // n_shards
+        dt = torch_dtype(cfg)
+        d, f = cfg.d_model, cfg.d_ff
+        wg = torch.empty((per, f, d), dtype=dt, device=x.device)
+        wu = torch.empty((per, f, d), dtype=dt, device=x.device)
+        wd = torch.empty((per, d, f), dtype=dt, device=x.device)
+
+        def put(i):
+            w = li.expert(shard * per + i)
+            wg[i].copy_(host_to_device(w[0], cfg, x.device))
+            wu[i].copy_(host_to_device(w[1], cfg, x.device))
+            wd[i].copy_(host_to_device(w[2], cfg, x.device))
+
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max(1, threads)) as ex:
+            list(ex.map(put, range(per)))
+        return cls(cfg, n_shards, shard, x, wg, wu, wd, tok, local_expert)
+
+    def forward(self, stream=None):
+        binding.moe_expert_shard_forward(self.cfg, self.x_recv, self.local_expert, self.w_gate, self.w_up,
+                                         self.w_down, self.y_send, self.ws, stream)
+        return self.y_send

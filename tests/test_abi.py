@@ -122,6 +122,22 @@ def test_entry_points_reject_bad_arguments_before_touching_the_device():
 
 
 @lib_built
+def test_expert_shard_rejects_bad_arguments_before_touching_the_device():
+    lib = binding.load_library()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    args = (fake, fake, fake, fake, fake, fake, fake)
+    ok = _cfg(top_k=1)
+    # a shard runs top-1 rows, dropless, without shared experts
+    for bad in (_cfg(top_k=2), _cfg(top_k=1, capacity_factor=1.25), _cfg(top_k=1, n_shared=1, d_ff_shared=128)):
+        assert lib.moe_expert_shard_forward(ctypes.byref(bad), *args, 1 << 40, None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_shard_forward(ctypes.byref(ok), fake, None, fake, fake, fake, fake, fake, 1 << 40,
+                                        None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_shard_forward(ctypes.byref(ok), *args, 16, None) == binding.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_shard_forward(ctypes.byref(_cfg(T=0, top_k=1)), None, None, None, None, None, None,
+                                        None, 0, None) == binding.MOE_OK
+
+
+@lib_built
 @pytest.mark.parametrize("cfg", list(configs.ALL.values()), ids=lambda c: c.name)
 def test_capacity_and_max_kept_match_the_oracle(cfg):
     C = oracle.expert_capacity(cfg.capacity_factor, cfg.T, cfg.top_k, cfg.n_experts)
