@@ -11,6 +11,10 @@ d=4096, f=14336, E=8, top-2, bf16). Prints ONE JSON line (rank 0):
              (4 d f N_kept) / its average launch time, HIP events recorded around that
              launch on the layer's stream inside the timed steps, against 2.5 PFLOP/s
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+Decode workloads (T <= 64) take the weight-streaming kernels, which are HBM-bound: there the
+roofline is the gated launch's algorithmic bytes (touched experts' gate and up weights as
+stored, token rows in, h out) per launch time, against 8 TB/s. The mixtral_decode_fp8_*
+workloads run the same layer with FP8 E4M3 expert weights (moe_layer_forward_fp8).
 """
 from __future__ import annotations
 
@@ -141,7 +145,7 @@ def shard_bench(args, w):
     flops_gate_up = 4.0 * cfg.d_model * cfg.d_ff * R
     if cfg.dtype == "bf16" and R <= SMALL_BATCH_TOKENS:
         touched = int((loads > 0).sum())
-        bytes_gate_up = 2.0 * cfg.d_model * cfg.d_ff * es * touched + R * cfg.d_model * es + R * cfg.d_ff * es
+        bytes_gate_up = float(touched * cfg.gate_up_bytes(cfg.d_ff)) + R * cfg.d_model * es + R * cfg.d_ff * es
         achieved = bytes_gate_up / (gate_up_ms.mean() * 1e-3) / 1e9
         roofline = {"kernel": "small_m_kernel<gated> (weight-streaming gate/up + SiLU*mul)", "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -192,8 +196,15 @@ def cpu_baseline(li, n_tokens: int):
     c = li.cfg
     x = li.values(li.x[:n_tokens])
     wr = li.values(li.w_router)
-    experts = [li.expert_values(e) for e in range(c.n_experts)]  # input generation: untimed
-    shared = [li.shared_values(s) for s in range(c.n_shared)]
+    if c.fp8:
+        # codes and scales drawn untimed; the oracle decodes them inside the timed region
+        codes = [li.expert_fp8(e) for e in range(c.n_experts)]
+        scodes = [li.shared_fp8(s) for s in range(c.n_shared)]
+        experts = lambda e: oracle.fp8_expert(*codes[e])  # noqa: E731
+        shared = lambda s: oracle.fp8_expert(*scodes[s])  # noqa: E731
+    else:
+        experts = [li.expert_values(e) for e in range(c.n_experts)]  # input generation: untimed
+        shared = [li.shared_values(s) for s in range(c.n_shared)]
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
@@ -203,8 +214,9 @@ def cpu_baseline(li, n_tokens: int):
     dt = time.perf_counter() - t0
     del experts
     return dict(value=n_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"first {n_tokens} of {c.T} tokens of {c.name}, all {c.n_experts} experts' "
-                       f"weights widened to float64 inside the timed region; {dt:.1f} s",
+                sample=f"first {n_tokens} of {c.T} tokens of {c.name}, the chosen experts' "
+                       f"weights {'decoded from FP8' if c.fp8 else 'widened'} to float64 inside the timed "
+                       f"region; {dt:.1f} s",
                 seconds=round(dt, 2))
 
 
@@ -270,14 +282,16 @@ def main():
     small_batch = cfg.dtype == "bf16" and cfg.T <= SMALL_BATCH_TOKENS
     if small_batch:
         # weight-streaming path: HBM-bound; algorithmic bytes of the gated launch = the touched
-        # experts' gate and up weights (+ shared), the token rows read, the h rows written
-        bytes_gate_up = (2.0 * cfg.d_model * cfg.d_ff * es * touched
-                         + 2.0 * cfg.d_model * cfg.d_ff_shared * es * cfg.n_shared
+        # experts' gate and up weights as stored (+ shared; FP8: codes and row scales), the
+        # token rows read, the h rows written
+        bytes_gate_up = (float(touched * cfg.gate_up_bytes(cfg.d_ff))
+                         + cfg.n_shared * cfg.gate_up_bytes(cfg.d_ff_shared)
                          + cfg.T * cfg.d_model * es + n_kept * cfg.d_ff * es
                          + cfg.n_shared * cfg.T * cfg.d_ff_shared * es)
         achieved = bytes_gate_up / (gate_up_ms.mean() * 1e-3) / 1e9
         roofline = {
-            "kernel": "small_m_kernel<gated> (weight-streaming gate/up + SiLU*mul)",
+            "kernel": ("small_m_kernel<gated, fp8>" if cfg.fp8 else "small_m_kernel<gated>")
+            + " (weight-streaming gate/up + SiLU*mul)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -301,7 +315,8 @@ def main():
             "flops_per_launch": flops_gate_up,
         }
     # whole-layer algorithmic bytes (weights of touched experts, router, x in and y out)
-    layer_bytes = (3.0 * cfg.d_model * cfg.d_ff * es * touched + 3.0 * cfg.d_model * cfg.d_ff_shared * es * cfg.n_shared
+    layer_bytes = (float(touched * cfg.expert_weight_bytes())
+                   + cfg.n_shared * (cfg.gate_up_bytes(cfg.d_ff_shared) + cfg.down_bytes(cfg.d_ff_shared))
                    + cfg.d_model * cfg.n_experts * es + 2.0 * cfg.T * cfg.d_model * es)
     out = {
         "metric": METRIC,
@@ -319,7 +334,8 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k, "gating": cfg.gating,
                    "capacity_factor": cfg.capacity_factor, "n_shared": cfg.n_shared,
-                   "d_ff_shared": cfg.d_ff_shared, "parallelism": "single GPU"},
+                   "d_ff_shared": cfg.d_ff_shared, "expert_weights": "fp8_e4m3" if cfg.fp8 else cfg.dtype,
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "layer": {
             "step_ms_p50": round(float(np.percentile(step_ms, 50)), 4),

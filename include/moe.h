@@ -129,12 +129,12 @@ MOE_API moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, i
                        int32_t* offsets, int32_t* sorted_slot, int32_t* pos, uint8_t* drop_mask,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Grouped expert MLP (klaylearn: "grouped GEMMs on each expert's batch"; techbonafide
+/* Grouped expert MLP (klaylearn: one grouped GEMM over the batch of each expert; techbonafide
  * "Experts as Specialized Subnetworks": an expert is a feed-forward block). For every
  * routed expert e and grouped position p in [offsets[e], offsets[e+1]):
  *   v = x[sorted_slot[p] / k];  y_perm[p] = (silu(v . Wg_e) * (v . Wu_e)) . Wd_e
- * and for every shared expert s and token t (pages' "The router": shared experts every
- * token always visits):  y_shared[s][t] = (silu(x_t . Wg_s) * (x_t . Wu_s)) . Wd_s.
+ * and for every shared expert s and token t (pages' "The router": a shared expert runs on
+ * every token, without a gate):  y_shared[s][t] = (silu(x_t . Wg_s) * (x_t . Wu_s)) . Wd_s.
  * y_perm [max_kept][d]; y_shared [n_shared][T][d] (required iff n_shared > 0, as are
  * ws_gate/ws_up/ws_down). The intermediate silu(.)*(.) is rounded to dtype.
  * Needs ws of MOE_OP_GROUPED_MLP bytes. */
@@ -182,6 +182,52 @@ MOE_API moe_status moe_expert_shard_forward(const moe_config* cfg, const void* x
                                     const int32_t* local_expert, const void* w_gate,
                                     const void* w_up, const void* w_down, void* y_send, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/* FP8 expert weights (pages: shubhamtatvamasi.com/llm-inference/moe, "Memory vs compute,
+ * quantified": in FP8 the weights take half their BF16 bytes, and small-batch decode time is
+ * the time to read the touched experts' weights; shipai.vats.cc "Mixture of Experts (MoE)",
+ * table "Production reality: serving MoE is not free": quantising experts is a serving
+ * lever whose error differs per expert, so each expert keeps its own scales here).
+ * One expert matrix is stored as OCP FP8 E4M3 codes, one byte per element (sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is subnormal, 2^-6 * m/8;
+ * no infinities; 0x7F and 0xFF are NaN; largest finite value 448), in the layouts of the
+ * dtype weights, with one float scale per output row (out feature) of each expert:
+ *   W[n][i] = scale[n] * e4m3(code[n][i]).
+ * For the routed experts n ranges over E experts and f = d_ff, for the shared experts over
+ * n_shared experts and f = d_ff_shared:
+ *   w_gate, w_up [n][f][d] codes   w_down [n][d][f] codes
+ *   scale_gate, scale_up [n][f]    scale_down [n][d]
+ * The struct is a host object; its members are device pointers, all required and 16-byte
+ * aligned (MOE_ERR_INVALID_ARG otherwise). Scales are finite; codes are never NaN codes. */
+typedef struct moe_fp8_weights {
+  const uint8_t* w_gate;
+  const uint8_t* w_up;
+  const uint8_t* w_down;
+  const float* scale_gate;
+  const float* scale_up;
+  const float* scale_down;
+} moe_fp8_weights;
+
+/* moe_grouped_mlp with FP8 expert weights: the same outputs, each weight element being the
+ * value it encodes times its row's scale. Activations (x, y_perm, y_shared, the
+ * intermediate) stay cfg->dtype, which must be MOE_BF16. Each dot product runs over the
+ * exact E4M3 values with an fp32 accumulator; the row's scale multiplies the sum.
+ * FP8 weights are meant for decode, where reading the weights is the whole cost: the batch
+ * must take the weight-streaming kernels, cfg->T <= 64; larger T, or dtype MOE_F32,
+ * returns MOE_ERR_UNSUPPORTED. `shared` (with y_shared) is required when n_shared > 0 and
+ * ignored otherwise. Workspace: moe_workspace_size(cfg, MOE_OP_GROUPED_MLP). */
+MOE_API moe_status moe_grouped_mlp_fp8(const moe_config* cfg, const void* x, const int32_t* sorted_slot,
+                               const int32_t* offsets, const moe_fp8_weights* experts,
+                               const moe_fp8_weights* shared, void* y_perm, void* y_shared, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* moe_layer_forward with FP8 expert weights (router weight in cfg->dtype, as before), under
+ * the restrictions of moe_grouped_mlp_fp8. The same results as moe_route, moe_permute,
+ * moe_grouped_mlp_fp8 and moe_combine called in turn. Workspace: MOE_OP_LAYER bytes. */
+MOE_API moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, const void* w_router,
+                                 const float* router_bias, const moe_fp8_weights* experts,
+                                 const moe_fp8_weights* shared, void* y, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* Instrumentation, for measuring one kernel inside a layer call. The next launch of
  * `kernel` (MOE_KERNEL_*) made by any entry point called on THIS host thread is bracketed

@@ -37,6 +37,14 @@ Readings where the pages are silent (each is listed with its reason in the desig
 
 Weight layout (out-features-major): router [E][d]; gate, up [E][f][d]; down [E][d][f].
 The products are v . Wg^T etc., i.e. the row-vector y = x . W of the d x f matrices.
+
+FP8 expert weights (shubhamtatvamasi.com, "Memory vs compute, quantified": FP8 halves the
+weight bytes of BF16; shipai.vats.cc, "Production reality: serving MoE is not free":
+quantisation error differs per expert). The pages fix no format; the reading taken is OCP
+E4M3 codes with one scale per output row of each expert matrix. ``e4m3_value`` decodes
+the format from its definition and ``dequantize_rows`` applies the scales; the grouped MLP
+then runs on those exact values, so an FP8 layer is the plain layer on dequantised
+weights.
 """
 from __future__ import annotations
 
@@ -73,7 +81,7 @@ def router_logits(x, w_router, bias=None) -> np.ndarray:
 # ---------------------------------------------------------------- step 2: top-k
 def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
     """The k highest-scoring experts per token, ordered by descending logit, ties to the
-    lower expert index ("keeps the top-k"). Returns int64 [T, k]."""
+    lower expert index (the router retains the k best). Returns int64 [T, k]."""
     T, E = logits.shape
     if not 1 <= k <= E:
         raise ValueError("need 1 <= k <= E")
@@ -177,6 +185,36 @@ def grouped_mlp(x, sorted_slot, offsets, k: int, experts: ExpertSource) -> np.nd
 def shared_mlp(x, shared: ExpertSource, n_shared: int) -> np.ndarray:
     """Every shared expert's FFN over all tokens: [n_shared, T, d]."""
     return np.stack([swiglu_ffn(x, *_expert(shared, s)) for s in range(n_shared)])
+
+
+# ---------------------------------------------------------------- FP8 expert weights
+def e4m3_value(codes) -> np.ndarray:
+    """The real number each OCP FP8 E4M3 code denotes, in float64 (exact).
+
+    Byte = sign bit | 4-bit exponent field E | 3-bit mantissa field M, exponent bias 7:
+      E == 0:            (-1)^s * 2^-6 * M/8        (zero and subnormals)
+      E in 1..15:        (-1)^s * 2^(E-7) * (1 + M/8)
+    except E == 15 with M == 7 (0x7F, 0xFF), which is NaN; the format has no infinities,
+    so 0x7E = 2^8 * 1.75 = 448 is the largest value. (Pages: shubhamtatvamasi.com, "Memory
+    vs compute, quantified": FP8 weights take one byte per parameter.)"""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    neg = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(neg == 1, -mag, mag)
+
+
+def dequantize_rows(codes, scale) -> np.ndarray:
+    """W[n, i] = scale[n] * e4m3(code[n, i]): one scale per output row (stored row)."""
+    return _f64(scale)[:, None] * e4m3_value(codes)
+
+
+def fp8_expert(codes_gate, codes_up, codes_down, scale_gate, scale_up, scale_down):
+    """The exact weight values (gate, up, down) of one FP8 expert, for swiglu_ffn."""
+    return (dequantize_rows(codes_gate, scale_gate), dequantize_rows(codes_up, scale_up),
+            dequantize_rows(codes_down, scale_down))
 
 
 # ---------------------------------------------------------------- step 7: combine

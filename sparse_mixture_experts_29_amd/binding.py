@@ -28,7 +28,8 @@ MOE_OP_PERMUTE, MOE_OP_GROUPED_MLP, MOE_OP_LAYER = 0, 1, 2
 # every function the header declares
 EXPORTS = ("moe_status_string", "moe_check_config", "moe_capacity", "moe_max_kept",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_mlp", "moe_combine",
-           "moe_layer_forward", "moe_expert_shard_forward", "moe_time_next_launch")
+           "moe_layer_forward", "moe_expert_shard_forward", "moe_grouped_mlp_fp8",
+           "moe_layer_forward_fp8", "moe_time_next_launch")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -48,9 +49,18 @@ class MoeConfig(ctypes.Structure):
                 ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class MoeFp8Weights(ctypes.Structure):
+    """moe_fp8_weights: E4M3 codes [n][f][d], [n][f][d], [n][d][f] and per-row float scales
+    [n][f], [n][f], [n][d] (device pointers)."""
+    _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("scale_gate", ctypes.c_void_p), ("scale_up", ctypes.c_void_p),
+                ("scale_down", ctypes.c_void_p)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _C = ctypes.POINTER(MoeConfig)
+_F = ctypes.POINTER(MoeFp8Weights)
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -76,6 +86,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P]),
         "moe_layer_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_expert_shard_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "moe_grouped_mlp_fp8": (ctypes.c_int, [_C, _P, _P, _P, _F, _F, _P, _P, _P, sz, _P]),
+        "moe_layer_forward_fp8": (ctypes.c_int, [_C, _P, _P, _P, _F, _F, _P, _P, sz, _P]),
         "moe_time_next_launch": (ctypes.c_int, [ctypes.c_int, _P, _P]),
     }
     for name, (res, args) in sig.items():
@@ -187,6 +199,35 @@ def moe_expert_shard_forward(cfg, x_recv, local_expert, w_gate, w_up, w_down, y_
     _check(load_library().moe_expert_shard_forward(
         ctypes.byref(_cfg(cfg)), _ptr(x_recv), _ptr(local_expert), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
         _ptr(y_send), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_expert_shard_forward")
+
+
+def fp8_weights(w) -> Optional[MoeFp8Weights]:
+    """(w_gate, w_up, w_down, scale_gate, scale_up, scale_down) device tensors (codes as
+    uint8, scales as float32) -> moe_fp8_weights; None stays None."""
+    if w is None:
+        return None
+    if isinstance(w, MoeFp8Weights):
+        return w
+    return MoeFp8Weights(*[_ptr(t) for t in w])
+
+
+def _byref_opt(s):
+    return None if s is None else ctypes.byref(s)
+
+
+def moe_grouped_mlp_fp8(cfg, x, sorted_slot, offsets, experts, shared, y_perm, y_shared, ws, stream=None):
+    """experts / shared: the six tensors of moe_fp8_weights (shared None without shared experts)."""
+    _check(load_library().moe_grouped_mlp_fp8(
+        ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(sorted_slot), _ptr(offsets), _byref_opt(fp8_weights(experts)),
+        _byref_opt(fp8_weights(shared)), _ptr(y_perm), _ptr(y_shared), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "moe_grouped_mlp_fp8")
+
+
+def moe_layer_forward_fp8(cfg, x, w_router, router_bias, experts, shared, y, ws, stream=None):
+    _check(load_library().moe_layer_forward_fp8(
+        ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias), _byref_opt(fp8_weights(experts)),
+        _byref_opt(fp8_weights(shared)), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "moe_layer_forward_fp8")
 
 
 def moe_time_next_launch(kernel: int, begin_event, end_event) -> None:

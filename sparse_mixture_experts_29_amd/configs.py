@@ -6,8 +6,9 @@ model width d, expert width f, E routed experts, top-k, the gating function
 (<= 0 means dropless) and optional always-on shared experts ("Mixture of Experts",
 shubhamtatvamasi.com, sections "The router" and "Load imbalance").
 
-The named workloads are the five shapes this library is checked and measured on.
-They hold shapes and seeds only; the values themselves come from ``inputs``.
+The named workloads are the five shapes this library is checked and measured on, plus
+the decode shape with FP8 expert weights. They hold shapes and seeds only; the values
+themselves come from ``inputs``.
 """
 from __future__ import annotations
 
@@ -35,6 +36,9 @@ class LayerConfig:
     router_bias: str = "none"  # "none" | "zipf" | "normal"
     bias_scale: float = 0.0  # zipf: exponent s; normal: std
     x_stream: int = 0  # index of x's random stream (decode sweeps use T)
+    # expert weights: "dtype" (stored in `dtype`) or "fp8_e4m3" (one-byte E4M3 codes and one
+    # float32 scale per output row; activations and the router stay in `dtype`)
+    weights: str = "dtype"
 
     @property
     def dropless(self) -> bool:
@@ -58,12 +62,30 @@ class LayerConfig:
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
 
+    @property
+    def fp8(self) -> bool:
+        return self.weights == "fp8_e4m3"
+
+    def matrix_bytes(self, rows: int, cols: int) -> int:
+        """Stored bytes of one expert matrix with `rows` output rows (codes + row scales for
+        FP8 weights)."""
+        if self.fp8:
+            return rows * cols + 4 * rows
+        return rows * cols * self.elem_bytes
+
+    def gate_up_bytes(self, f: int) -> int:
+        """gate and up matrices of one expert of width f."""
+        return 2 * self.matrix_bytes(f, self.d_model)
+
+    def down_bytes(self, f: int) -> int:
+        return self.matrix_bytes(self.d_model, f)
+
     def expert_weight_bytes(self) -> int:
-        return 3 * self.d_model * self.d_ff * self.elem_bytes
+        return self.gate_up_bytes(self.d_ff) + self.down_bytes(self.d_ff)
 
     def total_weight_bytes(self) -> int:
         b = self.n_experts * self.expert_weight_bytes()
-        b += self.n_shared * 3 * self.d_model * self.d_ff_shared * self.elem_bytes
+        b += self.n_shared * (self.gate_up_bytes(self.d_ff_shared) + self.down_bytes(self.d_ff_shared))
         b += self.n_experts * self.d_model * self.elem_bytes
         return b
 
@@ -84,6 +106,13 @@ def mixtral_decode(T: int) -> LayerConfig:
 
 DECODE_TS = (1, 4, 16, 64)
 
+
+def mixtral_decode_fp8(T: int) -> LayerConfig:
+    """The Mixtral-shaped decode layer with FP8 E4M3 expert weights (per-row scales); the
+    codes quantise the same draws as mixtral_decode(T)'s weights."""
+    return mixtral_decode(T).replace(name=f"mixtral_decode_fp8_T{T}_d4096_f14336_E8_k2", weights="fp8_e4m3")
+
+
 # Fine-grained Qwen3-30B-A3B-style layer: T=8192, d=2048, f=768, E=128, top-8, Zipf-skewed
 # router bias; run dropless and with capacity factor 1.25.
 QWEN3_FINE = LayerConfig("qwen3_fine_T8192_d2048_f768_E128_k8", T=8192, d_model=2048, d_ff=768,
@@ -96,7 +125,8 @@ DEEPSEEK_V3 = LayerConfig("deepseek_v3_T16384_d7168_f2048_E256_k8_s1", T=16384, 
                           d_ff_shared=2048, seed=4, router_bias="normal", bias_scale=0.5)
 
 ALL = {c.name: c for c in [TINY_FP32, MIXTRAL_PREFILL, *[mixtral_decode(t) for t in DECODE_TS],
-                           QWEN3_FINE, QWEN3_FINE_CF, DEEPSEEK_V3]}
+                           QWEN3_FINE, QWEN3_FINE_CF, DEEPSEEK_V3,
+                           *[mixtral_decode_fp8(t) for t in DECODE_TS]]}
 
 
 @dataclasses.dataclass(frozen=True)

@@ -89,6 +89,37 @@ LayerWs layer_layout(const Shape& s, void* base) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// FP8 weights: every member present and 16-byte aligned (the kernels read 16-byte vectors
+// of codes and of scales)
+moe_status check_fp8(const moe_fp8_weights* w) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  const void* p[6] = {w->w_gate, w->w_up, w->w_down, w->scale_gate, w->scale_up, w->scale_down};
+  for (const void* q : p)
+    if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// the FP8 entry points: bf16 activations, a batch the weight-streaming kernels take, and
+// valid weight structs (the shared one only when there are shared experts)
+moe_status fp8_args(const Shape& s, const moe_fp8_weights* experts, const moe_fp8_weights* shared,
+                    Fp8Scales* sc) {
+  if (s.dtype != MOE_BF16 || !use_small_m(s)) return MOE_ERR_UNSUPPORTED;
+  moe_status r = check_fp8(experts);
+  if (r == MOE_OK && s.n_shared > 0) r = check_fp8(shared);
+  if (r != MOE_OK) return r;
+  sc->gate = experts->scale_gate;
+  sc->up = experts->scale_up;
+  sc->down = experts->scale_down;
+  if (s.n_shared > 0) {
+    sc->shared_gate = shared->scale_gate;
+    sc->shared_up = shared->scale_up;
+    sc->shared_down = shared->scale_down;
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 TimingRequest& timing_request() {
@@ -270,6 +301,60 @@ moe_status moe_expert_shard_forward(const moe_config* cfg, const void* x_recv, c
     e = launch_grouped_mlp(s, x_recv, w.sorted_slot, w.offsets, w_gate, w_up, w_down, nullptr, nullptr, nullptr,
                            w.y_perm, nullptr, w.grouped_ws, st);
   if (e == hipSuccess) e = launch_combine(s, w.y_perm, w.pos, nullptr, nullptr, y_send, st);
+  return hip_status(e);
+}
+
+moe_status moe_grouped_mlp_fp8(const moe_config* cfg, const void* x, const int32_t* sorted_slot,
+                               const int32_t* offsets, const moe_fp8_weights* experts,
+                               const moe_fp8_weights* shared, void* y_perm, void* y_shared, void* ws,
+                               size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status r = to_shape(cfg, &s);
+  if (r != MOE_OK) return r;
+  if (s.dtype != MOE_BF16 || !use_small_m(s)) return MOE_ERR_UNSUPPORTED;
+  if (s.T == 0) return MOE_OK;
+  Fp8Scales sc;
+  r = fp8_args(s, experts, shared, &sc);
+  if (r != MOE_OK) return r;
+  if (!x || !sorted_slot || !offsets || !y_perm || !ws) return MOE_ERR_INVALID_ARG;
+  if (s.n_shared > 0 && !y_shared) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < grouped_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+  const moe_fp8_weights* sh = s.n_shared > 0 ? shared : nullptr;
+  return hip_status(launch_grouped_mlp(s, x, sorted_slot, offsets, experts->w_gate, experts->w_up,
+                                       experts->w_down, sh ? sh->w_gate : nullptr, sh ? sh->w_up : nullptr,
+                                       sh ? sh->w_down : nullptr, y_perm, y_shared, ws,
+                                       static_cast<hipStream_t>(stream), sc));
+}
+
+moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, const void* w_router,
+                                 const float* router_bias, const moe_fp8_weights* experts,
+                                 const moe_fp8_weights* shared, void* y, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  Shape s;
+  moe_status r = to_shape(cfg, &s);
+  if (r != MOE_OK) return r;
+  if (s.dtype != MOE_BF16 || !use_small_m(s)) return MOE_ERR_UNSUPPORTED;
+  if (s.T == 0) return MOE_OK;
+  Fp8Scales sc;
+  r = fp8_args(s, experts, shared, &sc);
+  if (r != MOE_OK) return r;
+  if (!x || !w_router || !y || !ws) return MOE_ERR_INVALID_ARG;
+  LayerWs w = layer_layout(s, ws);
+  if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const moe_fp8_weights* sh = s.n_shared > 0 ? shared : nullptr;
+  // the small-batch sequence of moe_layer_forward: the combine reads the down launch's
+  // split-K partials
+  hipError_t e = launch_route(s, x, w_router, router_bias, w.idx, w.gate, nullptr, st);
+  if (e == hipSuccess)
+    e = launch_permute(s, w.idx, w.counts, w.offsets, w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
+  if (e == hipSuccess)
+    e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, experts->w_gate, experts->w_up, experts->w_down,
+                           sh ? sh->w_gate : nullptr, sh ? sh->w_up : nullptr, sh ? sh->w_down : nullptr, nullptr,
+                           nullptr, w.grouped_ws, st, sc);
+  if (e == hipSuccess)
+    e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false), w.pos, w.gate,
+                                y, st);
   return hip_status(e);
 }
 

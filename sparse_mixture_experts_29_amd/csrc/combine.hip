@@ -3,7 +3,7 @@
 // Pages: shubhamtatvamasi.com/llm-inference/moe, Q&A "How does a top-k router work?" (the
 // token's output is the gate-weighted sum of its experts' outputs) and section "Load
 // imbalance" (a dropped pair skips its expert: it contributes nothing here);
-// klaylearn.com/glossary/mixture-of-experts, definition ("undoing the permutation").
+// klaylearn.com/glossary/mixture-of-experts, definition (the last step reverses the permutation).
 //
 // gate == nullptr means unit gates (the expert-parallel shard returns each row's output).
 // A gather, not a scatter: each block owns tokens and reads their k rows of y_perm, so

@@ -60,13 +60,26 @@ constexpr int kSmallMMaxRows = 64;
 bool use_small_m(const Shape& s);
 int small_m_splits(const Shape& s, bool gated);
 size_t small_m_ws_bytes(const Shape& s);
+// FP8 (E4M3) expert weights: per-output-row scales of the routed experts, [E][f] (gate, up)
+// and [E][d] (down), and of the shared experts, [n_s][f_s] and [n_s][d]; gate null for
+// weights in the layer's dtype.
+struct Fp8Scales {
+  const float* gate = nullptr;
+  const float* up = nullptr;
+  const float* down = nullptr;
+  const float* shared_gate = nullptr;
+  const float* shared_up = nullptr;
+  const float* shared_down = nullptr;
+};
+
 // y_perm == nullptr: stop after the down launch and leave the fp32 split-K partials in the
 // workspace (small_m_partials) for launch_combine_partials
 hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t* sorted_slot,
                                     const int32_t* offsets, const void* wg, const void* wu,
                                     const void* wd, const void* swg, const void* swu,
                                     const void* swd, void* h, void* hs, float* part,
-                                    void* y_perm, void* y_shared, hipStream_t st);
+                                    void* y_perm, void* y_shared, hipStream_t st,
+                                    const Fp8Scales& fp8 = Fp8Scales{});
 // the down launch's partials [splits][max_kept + n_s*T][d] inside the grouped-MLP workspace
 float* small_m_partials(const Shape& s, void* grouped_ws);
 // y from the partials: each kept slot's row is summed over the splits in order and rounded
@@ -80,10 +93,12 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
 hipError_t launch_permute(const Shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_slot, int32_t* pos, uint8_t* drop, void* ws,
                           hipStream_t st);
+// fp8: scales of FP8 expert weights (the weight-streaming path only: the caller checks use_small_m)
 hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sorted_slot,
                               const int32_t* offsets, const void* wg, const void* wu,
                               const void* wd, const void* swg, const void* swu, const void* swd,
-                              void* y_perm, void* y_shared, void* ws, hipStream_t st);
+                              void* y_perm, void* y_shared, void* ws, hipStream_t st,
+                              const Fp8Scales& fp8 = Fp8Scales{});
 hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos,
                           const float* gate, const void* y_shared, void* y, hipStream_t st);
 

@@ -1,10 +1,10 @@
 // Grouped expert MLP: for every expert, its batch of gathered token rows through the
 // SwiGLU block (silu(v Wg) * (v Wu)) Wd, as two grouped GEMM launches.
-// Pages: klaylearn.com/glossary/mixture-of-experts, definition ("running grouped GEMMs on
-// each expert's batch"); techbonafide.com "Mixture of Experts (MoE) Explained", section
+// Pages: klaylearn.com/glossary/mixture-of-experts, definition (one grouped GEMM over
+// the batch of each expert); techbonafide.com "Mixture of Experts (MoE) Explained", section
 // "Experts as Specialized Subnetworks" (an expert is a standard feed-forward block);
-// shubhamtatvamasi.com/llm-inference/moe, section "The router" (shared experts every token
-// always visits).
+// shubhamtatvamasi.com/llm-inference/moe, section "The router" (a shared expert runs on every
+// token, ungated).
 //
 // Groups: the E routed experts (rows = their slice of the grouped order, input row =
 // x[sorted_slot[p] / k]) and the n_s shared experts (rows = all T tokens, identity
@@ -731,11 +731,12 @@ int cu_count() {
 hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sorted_slot,
                               const int32_t* offsets, const void* wg, const void* wu,
                               const void* wd, const void* swg, const void* swu, const void* swd,
-                              void* y_perm, void* y_shared, void* ws, hipStream_t st) {
+                              void* y_perm, void* y_shared, void* ws, hipStream_t st, const Fp8Scales& fp8) {
   GroupedWs w = carve(s, ws);
   if (use_small_m(s))
     return launch_grouped_mlp_small(s, x, sorted_slot, offsets, wg, wu, wd, swg, swu, swd, w.h, w.hs,
-                                    w.part, y_perm, y_shared, st);
+                                    w.part, y_perm, y_shared, st, fp8);
+  if (fp8.gate) return hipErrorInvalidValue;  // FP8 weights: weight-streaming path only
   const int bm = tile_rows(s);
   const int64_t mb = m_tile_bound(s);
   int32_t* queues = w.n_tiles + 16;

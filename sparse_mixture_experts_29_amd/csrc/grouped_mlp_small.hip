@@ -31,10 +31,14 @@ struct SmallArgs {
   const bf16_t* in_s;          // shared input rows: x [T][K] or hs [n_s*T][K]
   const int32_t* sorted_slot;  // gated launch: routed rows gather x[sorted_slot[p] / k]
   const int32_t* offsets;      // [E+1]
-  const bf16_t* w0_r;          // [E][N_r][K_r]
-  const bf16_t* w1_r;
-  const bf16_t* w0_s;          // [n_s][N_s][K_s]
-  const bf16_t* w1_s;
+  const void* w0_r;            // [E][N_r][K_r] bf16, or FP8 E4M3 codes (one byte each)
+  const void* w1_r;
+  const void* w0_s;            // [n_s][N_s][K_s]
+  const void* w1_s;
+  const float* s0_r;           // FP8 weights: per-output-row scales [E][N_r] (else null)
+  const float* s1_r;
+  const float* s0_s;           // FP8 weights: shared experts' scales [n_s][N_s]
+  const float* s1_s;
   bf16_t* out_r;               // gated: h [max_kept][N_r]
   bf16_t* out_s;               // gated: hs [n_s*T][N_s]
   float* part;                 // K-split partials: gated [splits][rows][2][fw], down [splits][rows][N]
@@ -50,13 +54,38 @@ struct SmallArgs {
 // K loop and epilogue of one unit with NG (compile-time) token groups of 16. Operands of
 // K block i+D-1 (weights and token rows) are loaded while block i is multiplied: a ring of
 // D register sets, so no load waits on the one before it.
-template <bool GATED, int NG, int D>
-__device__ __forceinline__ void small_m_unit(const SmallArgs& a, const bf16_t* w0, const bf16_t* w1,
+// FP8 (E4M3) weights: a lane's 32 k values of a block are 32 bytes (two 16-byte loads) and
+// are widened to bf16 exactly (every E4M3 value is a bf16 value) right before the multiply;
+// the per-row scale multiplies the accumulator in the epilogue.
+template <bool GATED, int NG, int D, bool FP8>
+__device__ __forceinline__ void small_m_unit(const SmallArgs& a, const void* w0, const void* w1,
                                              const bf16_t* const (&xp)[2], int t0, int kbeg, int kend,
                                              int quad, int l16, int M, int r0, int gi, bool shared,
                                              int N, int n0, int split) {
+  constexpr int NW = FP8 ? 2 : 4;  // 16-byte weight loads per lane per block and matrix
   struct Ops {
-    u32x4 wa[4], wb[4], xv[NG][4];
+    u32x4 wa[NW], wb[NW], xv[NG][4];
+  };
+  // A operand c of a block (k = ko + 8c .. +8), from the raw weight registers; m zeroes the
+  // dead lanes of the tail block (FP8 code 0 is +0)
+  auto wop = [&](const u32x4 (&w)[NW], int c, unsigned m) -> bf16x8 {
+    if constexpr (!FP8) {
+      return __builtin_bit_cast(bf16x8, w[c] & m);
+    } else {
+      const u32x4 raw = w[c >> 1] & m;
+      const unsigned d0 = raw[(c & 1) * 2], d1 = raw[(c & 1) * 2 + 1];
+      const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+      const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+      const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+      const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+      return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+  };
+  auto wfull = [&](const u32x4 (&w)[NW], int c) -> bf16x8 {
+    if constexpr (!FP8)
+      return __builtin_bit_cast(bf16x8, w[c]);
+    else
+      return wop(w, c, 0xFFFFFFFFu);
   };
   f32x4 acc0[NG], acc1[NG];
 #pragma unroll
@@ -74,8 +103,15 @@ __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const bf16_t* w
     const int ko = kb + (full || quad < 2 ? quad * 32 : 0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      o.wa[c] = *reinterpret_cast<const u32x4*>(w0 + ko + c * 8);
-      if (GATED) o.wb[c] = *reinterpret_cast<const u32x4*>(w1 + ko + c * 8);
+      if constexpr (FP8) {
+        if (c < NW) {
+          o.wa[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w0) + ko + c * 16);
+          if (GATED) o.wb[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w1) + ko + c * 16);
+        }
+      } else {
+        o.wa[c] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(w0) + ko + c * 8);
+        if (GATED) o.wb[c] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(w1) + ko + c * 8);
+      }
 #pragma unroll
       for (int t = 0; t < NG; ++t) o.xv[t][c] = *reinterpret_cast<const u32x4*>(xp[t] + ko + c * 8);
     }
@@ -87,9 +123,8 @@ __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const bf16_t* w
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
         const bf16x8 x = __builtin_bit_cast(bf16x8, o.xv[t][c] & m);
-        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.wa[c] & m), x, acc0[t], 0, 0, 0);
-        if (GATED)
-          acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.wb[c] & m), x, acc1[t], 0, 0, 0);
+        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop(o.wa, c, m), x, acc0[t], 0, 0, 0);
+        if (GATED) acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop(o.wb, c, m), x, acc1[t], 0, 0, 0);
       }
   };
   auto mma_full = [&](const Ops& o) {
@@ -98,9 +133,8 @@ __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const bf16_t* w
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
         const bf16x8 x = __builtin_bit_cast(bf16x8, o.xv[t][c]);
-        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.wa[c]), x, acc0[t], 0, 0, 0);
-        if (GATED)
-          acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.wb[c]), x, acc1[t], 0, 0, 0);
+        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfull(o.wa, c), x, acc0[t], 0, 0, 0);
+        if (GATED) acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfull(o.wb, c), x, acc1[t], 0, 0, 0);
       }
   };
   const int nfull = (kend - kbeg) / 128;        // full 128-wide blocks
@@ -141,6 +175,17 @@ __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const bf16_t* w
   // column l16 of each group.
   const int ncol = n0 + quad * 4;
   if (ncol >= N) return;
+  if constexpr (FP8) {  // per-row scales of the FP8 weights
+    const float* sc0 = shared ? a.s0_s : a.s0_r;
+    const float* sc1 = shared ? a.s1_s : a.s1_r;
+    const float4 s0 = *reinterpret_cast<const float4*>(sc0 + static_cast<int64_t>(gi) * N + ncol);
+    const float4 s1 = GATED ? *reinterpret_cast<const float4*>(sc1 + static_cast<int64_t>(gi) * N + ncol) : s0;
+#pragma unroll
+    for (int t = 0; t < NG; ++t) {
+      acc0[t] = f32x4{acc0[t][0] * s0.x, acc0[t][1] * s0.y, acc0[t][2] * s0.z, acc0[t][3] * s0.w};
+      if (GATED) acc1[t] = f32x4{acc1[t][0] * s1.x, acc1[t][1] * s1.y, acc1[t][2] * s1.z, acc1[t][3] * s1.w};
+    }
+  }
 #pragma unroll
   for (int t = 0; t < NG; ++t) {
     const int tok = (t0 + t) * 16 + l16;
@@ -173,7 +218,7 @@ __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const bf16_t* w
 // group with more rows than NGW*16 is covered by `halves` passes, one per NGW token groups.
 // The half is the slowest unit index: in a typical small batch every group fits one half,
 // and the blocks of the other halves exit at once instead of idling inside working blocks.
-template <bool GATED, int NGW>
+template <bool GATED, int NGW, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void small_m_kernel(SmallArgs a) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (readfirstlane): everything derived from the unit stays in scalar registers
@@ -212,8 +257,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   const int l16 = lane & 15, quad = lane >> 4;
   const int n = min(n0 + l16, N - 1);
-  const bf16_t* w0 = (shared ? a.w0_s : a.w0_r) + (static_cast<int64_t>(gi) * N + n) * K;
-  const bf16_t* w1 = GATED ? (shared ? a.w1_s : a.w1_r) + (static_cast<int64_t>(gi) * N + n) * K : nullptr;
+  const int64_t wel = (static_cast<int64_t>(gi) * N + n) * K;  // element offset of the lane's row
+  const void* w0;
+  const void* w1 = nullptr;
+  if constexpr (FP8) {
+    w0 = static_cast<const uint8_t*>(shared ? a.w0_s : a.w0_r) + wel;
+    if (GATED) w1 = static_cast<const uint8_t*>(shared ? a.w1_s : a.w1_r) + wel;
+  } else {
+    w0 = static_cast<const bf16_t*>(shared ? a.w0_s : a.w0_r) + wel;
+    if (GATED) w1 = static_cast<const bf16_t*>(shared ? a.w1_s : a.w1_r) + wel;
+  }
   const bf16_t* in = shared ? a.in_s : a.in_r;
 
   const bf16_t* xp[2];
@@ -227,10 +280,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       src = GATED ? a.sorted_slot[r] / a.k : r;
     xp[t] = in + src * K;
   }
+  // FP8 blocks carry half the weight bytes: a deeper ring keeps as many bytes in flight
   if (NGW == 1 || ng <= 1)
-    small_m_unit<GATED, 1, 3>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split);
+    small_m_unit<GATED, 1, FP8 ? 5 : 3, FP8>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0,
+                                            split);
   else
-    small_m_unit<GATED, 2, 3>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split);
+    small_m_unit<GATED, 2, 3, FP8>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split);
 }
 
 // h = silu(sum of gate partials) * (sum of up partials), the sums over K splits in split
@@ -343,8 +398,9 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
                                     const int32_t* offsets, const void* wg, const void* wu,
                                     const void* wd, const void* swg, const void* swu,
                                     const void* swd, void* h, void* hs, float* part,
-                                    void* y_perm, void* y_shared, hipStream_t st) {
+                                    void* y_perm, void* y_shared, hipStream_t st, const Fp8Scales& fp8) {
   SmallArgs a{};
+  const bool f8 = fp8.gate != nullptr;
   a.sorted_slot = sorted_slot;
   a.offsets = offsets;
   a.E = s.E;
@@ -356,10 +412,10 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   // gated: h = silu(x Wg) * (x Wu)
   a.in_r = static_cast<const bf16_t*>(x);
   a.in_s = static_cast<const bf16_t*>(x);
-  a.w0_r = static_cast<const bf16_t*>(wg);
-  a.w1_r = static_cast<const bf16_t*>(wu);
-  a.w0_s = static_cast<const bf16_t*>(swg);
-  a.w1_s = static_cast<const bf16_t*>(swu);
+  a.w0_r = wg;
+  a.w1_r = wu;
+  a.w0_s = swg;
+  a.w1_s = swu;
   a.out_r = static_cast<bf16_t*>(h);
   a.out_s = static_cast<bf16_t*>(hs);
   a.N_r = s.f;
@@ -376,8 +432,14 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   const int groups16 = static_cast<int>((s.T + 15) / 16);
   const int ngw = groups16 <= 1 ? 1 : 2;
   a.halves = (groups16 + ngw - 1) / ngw;
-  auto kern_g = ngw == 1 ? small_m_kernel<true, 1> : small_m_kernel<true, 2>;
-  auto kern_d = ngw == 1 ? small_m_kernel<false, 1> : small_m_kernel<false, 2>;
+  auto kern_g = f8 ? (ngw == 1 ? small_m_kernel<true, 1, true> : small_m_kernel<true, 2, true>)
+                  : (ngw == 1 ? small_m_kernel<true, 1, false> : small_m_kernel<true, 2, false>);
+  auto kern_d = f8 ? (ngw == 1 ? small_m_kernel<false, 1, true> : small_m_kernel<false, 2, true>)
+                  : (ngw == 1 ? small_m_kernel<false, 1, false> : small_m_kernel<false, 2, false>);
+  a.s0_r = fp8.gate;
+  a.s1_r = fp8.up;
+  a.s0_s = fp8.shared_gate;
+  a.s1_s = fp8.shared_up;
   units *= a.halves;
   timing_begin(MOE_KERNEL_GATE_UP, st);
   hipLaunchKernelGGL(kern_g, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(kThreads), 0, st, a);
@@ -393,9 +455,13 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   a.sorted_slot = nullptr;
   a.in_r = static_cast<const bf16_t*>(h);
   a.in_s = static_cast<const bf16_t*>(hs);
-  a.w0_r = static_cast<const bf16_t*>(wd);
+  a.w0_r = wd;
   a.w1_r = nullptr;
-  a.w0_s = static_cast<const bf16_t*>(swd);
+  a.s0_r = fp8.down;
+  a.s1_r = nullptr;
+  a.s0_s = fp8.shared_down;
+  a.s1_s = nullptr;
+  a.w0_s = swd;
   a.w1_s = nullptr;
   a.part = part;
   a.N_r = s.d;

@@ -1,7 +1,7 @@
 // Permute: group the (token, slot) pairs by destination expert, stable in token order,
 // with an optional per-expert capacity that drops the overflow.
-// Pages: klaylearn.com/glossary/mixture-of-experts, definition ("permuting tokens by
-// destination expert"); shubhamtatvamasi.com/llm-inference/moe, section "Load imbalance"
+// Pages: klaylearn.com/glossary/mixture-of-experts, definition (tokens are regrouped
+// by the expert they go to); shubhamtatvamasi.com/llm-inference/moe, section "Load imbalance"
 // (capacity factor x ideal tokens; overflow skips the expert) and Q&A on capacity factor
 // (limit factor x (T.k/E)); dropless when no capacity is set.
 //

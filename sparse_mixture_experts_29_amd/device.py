@@ -44,10 +44,17 @@ class DeviceLayer:
         self.x = host_to_device(li.x, cfg, device)
         self.w_router = host_to_device(li.w_router, cfg, device)
         self.router_bias = None if li.router_bias is None else torch.from_numpy(li.router_bias).to(device)
+        self.s_gate = self.s_up = self.s_down = None  # FP8 row scales
+        self.ss_gate = self.ss_up = self.ss_down = None
         if weights_from is not None:
             o = weights_from.cfg
-            assert (o.seed, o.n_experts, o.d_model, o.d_ff, o.dtype) == (cfg.seed, E, d, f, cfg.dtype)
+            assert (o.seed, o.n_experts, o.d_model, o.d_ff, o.dtype, o.weights) == \
+                (cfg.seed, E, d, f, cfg.dtype, cfg.weights)
             self.w_gate, self.w_up, self.w_down = weights_from.w_gate, weights_from.w_up, weights_from.w_down
+            self.s_gate, self.s_up, self.s_down = weights_from.s_gate, weights_from.s_up, weights_from.s_down
+        elif cfg.fp8:
+            self.w_gate, self.w_up, self.w_down, self.s_gate, self.s_up, self.s_down = \
+                _upload_fp8(li, E, f, d, device, threads, shared=False)
         else:
             self.w_gate = torch.empty((E, f, d), dtype=dt, device=device)
             self.w_up = torch.empty((E, f, d), dtype=dt, device=device)
@@ -62,7 +69,10 @@ class DeviceLayer:
 
             li.for_each_expert(put, threads)
         self.ws_gate = self.ws_up = self.ws_down = None
-        if cfg.n_shared:
+        if cfg.n_shared and cfg.fp8:
+            self.ws_gate, self.ws_up, self.ws_down, self.ss_gate, self.ss_up, self.ss_down = \
+                _upload_fp8(li, cfg.n_shared, cfg.d_ff_shared, d, device, 1, shared=True)
+        elif cfg.n_shared:
             fs = cfg.d_ff_shared
             self.ws_gate = torch.empty((cfg.n_shared, fs, d), dtype=dt, device=device)
             self.ws_up = torch.empty((cfg.n_shared, fs, d), dtype=dt, device=device)
@@ -77,8 +87,22 @@ class DeviceLayer:
                               device=device)
         torch.cuda.synchronize(self.device)
 
+    def fp8_experts(self):
+        """The routed and shared moe_fp8_weights of an FP8 layer (shared None without)."""
+        ex = binding.fp8_weights((self.w_gate, self.w_up, self.w_down, self.s_gate, self.s_up, self.s_down))
+        sh = None
+        if self.cfg.n_shared:
+            sh = binding.fp8_weights((self.ws_gate, self.ws_up, self.ws_down, self.ss_gate, self.ss_up,
+                                      self.ss_down))
+        return ex, sh
+
     # ---------------------------------------------------------------- whole layer
     def forward(self, stream=None) -> torch.Tensor:
+        if self.cfg.fp8:
+            ex, sh = self.fp8_experts()
+            binding.moe_layer_forward_fp8(self.cfg, self.x, self.w_router, self.router_bias, ex, sh, self.y,
+                                          self.ws, stream)
+            return self.y
         binding.moe_layer_forward(self.cfg, self.x, self.w_router, self.router_bias, self.w_gate,
                                   self.w_up, self.w_down, self.ws_gate, self.ws_up, self.ws_down,
                                   self.y, self.ws, stream)
@@ -119,12 +143,35 @@ class DeviceLayer:
                             b["sorted_slot"], b["pos"], b["drop"], b["permute_ws"], stream)
 
     def grouped_mlp(self, b: dict, stream=None):
+        if self.cfg.fp8:
+            ex, sh = self.fp8_experts()
+            binding.moe_grouped_mlp_fp8(self.cfg, self.x, b["sorted_slot"], b["offsets"], ex, sh, b["y_perm"],
+                                        b["y_shared"], b["grouped_ws"], stream)
+            return
         binding.moe_grouped_mlp(self.cfg, self.x, b["sorted_slot"], b["offsets"], self.w_gate, self.w_up,
                                 self.w_down, self.ws_gate, self.ws_up, self.ws_down, b["y_perm"],
                                 b["y_shared"], b["grouped_ws"], stream)
 
     def combine(self, b: dict, stream=None):
         binding.moe_combine(self.cfg, b["y_perm"], b["pos"], b["gate"], b["y_shared"], b["y"], stream)
+
+
+def _upload_fp8(li: LayerInputs, n: int, f: int, d: int, device, threads: int, shared: bool):
+    """Codes (uint8) and row scales (float32) of n FP8 experts of width f, uploaded one expert
+    at a time: gate, up [n][f][d], down [n][d][f], scales [n][f], [n][f], [n][d]."""
+    u8 = dict(dtype=torch.uint8, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    t = [torch.empty((n, f, d), **u8), torch.empty((n, f, d), **u8), torch.empty((n, d, f), **u8),
+         torch.empty((n, f), **f32), torch.empty((n, f), **f32), torch.empty((n, d), **f32)]
+    lock = threading.Lock()
+
+    def put(e, w):
+        with lock:
+            for dst, src in zip(t, w):
+                dst[e].copy_(torch.from_numpy(np.ascontiguousarray(src)))
+
+    li.for_each_expert(put, threads, shared=shared)
+    return tuple(t)
 
 
 def shard_rows(idx, n_shards: int, shard: int, n_experts: int):

@@ -12,6 +12,10 @@ so that experts can be produced one at a time and regenerated on demand):
   (std = 1/sqrt(fan_in));
 * router bias: none; "zipf" = a seeded permutation gives each expert a rank r in 1..E,
   w = r^-s, and the bias is w min-max scaled linearly onto [-2, 2]; "normal" = N(0, std).
+* FP8 expert weights (weights == "fp8_e4m3"): the same float32 draws, quantised per output
+  row: scale = max |row| / 448 (the largest E4M3 value), codes = torch's float8_e4m3fn
+  cast (round to nearest) of row / scale. This is how a checkpoint would be converted; the
+  library and the oracle only ever see the codes and the scales.
 
 Memory layout of every weight is out-features-major (the layout of a linear layer's
 weight): router [E][d], gate and up [E][f][d], down [E][d][f], shared gate/up
@@ -42,6 +46,21 @@ def to_bf16_bits(a: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns -> the float32 values they denote (exact)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+E4M3_MAX = 448.0
+
+
+def quantize_rows_e4m3(a: np.ndarray):
+    """float32 [rows, cols] -> (E4M3 codes uint8 [rows, cols], float32 scale [rows]): one
+    scale per row, max |row| / 448 (1 for an all-zero row), codes = round-to-nearest cast of
+    row / scale (clamped to +-448 first, so no code is NaN)."""
+    import torch
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    amax = np.abs(a).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = torch.from_numpy(a / scale[:, None]).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy(), scale
 
 
 def _normal(seed: int, tag: int, index: int, shape, std: float) -> np.ndarray:
@@ -76,7 +95,19 @@ class LayerInputs:
         return wg, wu, wd
 
     def expert_values(self, e: int):
+        if self.cfg.fp8:
+            raise ValueError("FP8 expert weights are codes and scales: decode them with the oracle")
         return tuple(self.values(w) for w in self.expert(e))
+
+    def expert_fp8(self, e: int):
+        """FP8 routed expert e: (gate codes [f][d], up codes [f][d], down codes [d][f],
+        gate scale [f], up scale [f], down scale [d])."""
+        c = self.cfg
+        sd, sf = 1.0 / math.sqrt(c.d_model), 1.0 / math.sqrt(c.d_ff)
+        cg, sg = quantize_rows_e4m3(_normal(c.seed, TAG_WG, e, (c.d_ff, c.d_model), sd))
+        cu, su = quantize_rows_e4m3(_normal(c.seed, TAG_WU, e, (c.d_ff, c.d_model), sd))
+        cdn, sdn = quantize_rows_e4m3(_normal(c.seed, TAG_WD, e, (c.d_model, c.d_ff), sf))
+        return cg, cu, cdn, sg, su, sdn
 
     # ---- shared experts ------------------------------------------------
     def shared(self, s: int):
@@ -88,15 +119,30 @@ class LayerInputs:
         return wg, wu, wd
 
     def shared_values(self, s: int):
+        if self.cfg.fp8:
+            raise ValueError("FP8 expert weights are codes and scales: decode them with the oracle")
         return tuple(self.values(w) for w in self.shared(s))
+
+    def shared_fp8(self, s: int):
+        """FP8 shared expert s, in the order of expert_fp8."""
+        c = self.cfg
+        sd, sf = 1.0 / math.sqrt(c.d_model), 1.0 / math.sqrt(c.d_ff_shared)
+        cg, sg = quantize_rows_e4m3(_normal(c.seed, TAG_SWG, s, (c.d_ff_shared, c.d_model), sd))
+        cu, su = quantize_rows_e4m3(_normal(c.seed, TAG_SWU, s, (c.d_ff_shared, c.d_model), sd))
+        cdn, sdn = quantize_rows_e4m3(_normal(c.seed, TAG_SWD, s, (c.d_model, c.d_ff_shared), sf))
+        return cg, cu, cdn, sg, su, sdn
 
     # ---- bulk production ---------------------------------------------
     def for_each_expert(self, fn: Callable[[int, tuple], None], threads: int = 8,
                         shared: bool = False) -> None:
         """Call fn(index, (wg, wu, wd)) for every routed (or shared) expert, producing
-        them on ``threads`` threads (numpy releases the GIL while drawing)."""
+        them on ``threads`` threads (numpy releases the GIL while drawing). FP8 layers pass
+        the six arrays of expert_fp8 instead."""
         n = self.cfg.n_shared if shared else self.cfg.n_experts
-        make = self.shared if shared else self.expert
+        if self.cfg.fp8:
+            make = self.shared_fp8 if shared else self.expert_fp8
+        else:
+            make = self.shared if shared else self.expert
 
         def work(i):
             fn(i, make(i))

@@ -60,7 +60,10 @@ def assert_close_output(got: np.ndarray, want: np.ndarray, dtype: str, what: str
 
 
 def oracle_weights(li: LayerInputs):
-    """Exact values of routed and shared experts, produced on demand (oracle upcasts)."""
+    """Exact values of routed and shared experts, produced on demand (oracle upcasts; FP8
+    codes and scales are decoded by the oracle)."""
+    if li.cfg.fp8:
+        return (lambda e: oracle.fp8_expert(*li.expert_fp8(e))), (lambda s: oracle.fp8_expert(*li.shared_fp8(s)))
     return (lambda e: li.expert_values(e)), (lambda s: li.shared_values(s))
 
 
@@ -186,6 +189,7 @@ def check_layer_sampled(li: LayerInputs, dev: DeviceLayer, n_tokens: int = 8, n_
     picks = [int(nonempty[np.argmax(counts[nonempty])]), int(nonempty[np.argmin(counts[nonempty])])]
     picks += [int(e) for e in rng.choice(nonempty, size=max(0, n_experts - 2), replace=False)]
     y_perm = b["y_perm"]
+    experts, shared = oracle_weights(li)
     worst = 0.0
     for e in dict.fromkeys(picks):
         a0, a1 = int(off[e]), int(off[e + 1])
@@ -193,18 +197,17 @@ def check_layer_sampled(li: LayerInputs, dev: DeviceLayer, n_tokens: int = 8, n_
         h = rows_per_expert // 3
         rows = np.unique(np.concatenate([np.arange(a0, min(a1, a0 + h)), np.arange(max(a0, a1 - h), a1),
                                          rng.integers(a0, a1, size=min(n, h))]))
-        want = oracle.swiglu_ffn(x[p["sorted_slot"][rows] // c.top_k], *li.expert_values(e))
+        want = oracle.swiglu_ffn(x[p["sorted_slot"][rows] // c.top_k], *experts(e))
         got = P_host_rows(y_perm, rows)
         worst = max(worst, assert_close_output(got, want, c.dtype, f"y_perm rows of expert {e} ({n} rows)"))
     toks = np.unique(np.concatenate([[0, c.T - 1], rng.integers(0, c.T, size=n_tokens)]))
     keep = (p["drop"].reshape(c.T, c.top_k) == 0)[toks]
     if c.n_shared:
-        ys = oracle.shared_mlp(x[toks], lambda s: li.shared_values(s), c.n_shared)
+        ys = oracle.shared_mlp(x[toks], shared, c.n_shared)
         for s_ in range(c.n_shared):
             assert_close_output(b["y_shared"][s_][torch.as_tensor(toks, device=b["y_shared"].device)].float().cpu().numpy(),
                                 ys[s_], c.dtype, f"y_shared[{s_}]")
-    want_y = oracle.token_outputs(x[toks], r["idx"][toks], r["gate"][toks], keep, lambda e: li.expert_values(e),
-                                  lambda s: li.shared_values(s), c.n_shared)
+    want_y = oracle.token_outputs(x[toks], r["idx"][toks], r["gate"][toks], keep, experts, shared, c.n_shared)
     y_rows = b["y"][torch.as_tensor(toks, device=b["y"].device)]
     e2 = assert_close_output(host(y_rows), want_y, c.dtype, "y (sampled tokens)")
     yl = dev.forward()

@@ -154,3 +154,68 @@ def test_capacity_and_max_kept_match_the_oracle(cfg):
 def test_capacity_rounding_agrees_with_the_oracle(cf, T, k, E):
     c = _cfg(T=T, top_k=k, n_experts=E, capacity_factor=cf)
     assert binding.moe_capacity(c) == oracle.expert_capacity(cf, T, k, E)
+
+
+def test_fp8_weights_struct_layout(tmp_path):
+    src = tmp_path / "f.c"
+    src.write_text('#include "moe.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   "int main(void){ printf(\"%zu %zu %zu\\n\", sizeof(moe_fp8_weights),"
+                   " offsetof(moe_fp8_weights, w_down), offsetof(moe_fp8_weights, scale_down)); return 0; }\n")
+    exe = tmp_path / "f"
+    subprocess.run(["gcc", "-Wall", "-Werror", f"-I{os.path.dirname(HEADER)}", str(src), "-o", str(exe)], check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    W = binding.MoeFp8Weights
+    assert out == [ctypes.sizeof(W), W.w_down.offset, W.scale_down.offset]
+
+
+def _fp8(base=0x1000, **kw):
+    """A moe_fp8_weights of fake, 16-byte aligned device addresses (never dereferenced)."""
+    f = dict(w_gate=base, w_up=base + 0x100, w_down=base + 0x200, scale_gate=base + 0x300,
+             scale_up=base + 0x400, scale_down=base + 0x500)
+    f.update(kw)
+    return binding.MoeFp8Weights(**f)
+
+
+@lib_built
+def test_fp8_entry_points_reject_bad_arguments_before_touching_the_device():
+    lib = binding.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    ex = ctypes.byref(_fp8())
+    big = 1 << 40
+
+    def layer(cfg, experts=ex, shared=None, ws_bytes=big):
+        return lib.moe_layer_forward_fp8(ctypes.byref(cfg), fake, fake, None, experts, shared, fake, fake, ws_bytes,
+                                         None)
+
+    def grouped(cfg, experts=ex, shared=None, y_shared=None, ws_bytes=big):
+        return lib.moe_grouped_mlp_fp8(ctypes.byref(cfg), fake, fake, fake, experts, shared, fake, y_shared, fake,
+                                       ws_bytes, None)
+
+    small = _cfg(T=64)
+    # FP8 weights run on the weight-streaming path only: bf16 activations, at most 64 tokens
+    assert layer(_cfg(T=65)) == binding.MOE_ERR_UNSUPPORTED
+    assert grouped(_cfg(T=4096)) == binding.MOE_ERR_UNSUPPORTED
+    assert layer(_cfg(T=4, dtype=binding.MOE_F32)) == binding.MOE_ERR_UNSUPPORTED
+    # every member present and 16-byte aligned
+    assert layer(small, experts=None) == binding.MOE_ERR_INVALID_ARG
+    assert layer(small, experts=ctypes.byref(_fp8(scale_up=None))) == binding.MOE_ERR_INVALID_ARG
+    assert layer(small, experts=ctypes.byref(_fp8(w_down=0x1008))) == binding.MOE_ERR_INVALID_ARG
+    assert grouped(small, experts=ctypes.byref(_fp8(scale_gate=0x1004))) == binding.MOE_ERR_INVALID_ARG
+    # the shared struct (and y_shared) are required with shared experts, ignored without
+    sh_cfg = _cfg(T=8, n_shared=1, d_ff_shared=128)
+    assert layer(sh_cfg) == binding.MOE_ERR_INVALID_ARG
+    assert grouped(sh_cfg, shared=ex) == binding.MOE_ERR_INVALID_ARG  # no y_shared
+    assert layer(sh_cfg, shared=ctypes.byref(_fp8(w_up=None))) == binding.MOE_ERR_INVALID_ARG
+    assert layer(small, shared=ctypes.byref(_fp8(w_up=None)), ws_bytes=16) == binding.MOE_ERR_WORKSPACE
+    assert grouped(small, ws_bytes=16) == binding.MOE_ERR_WORKSPACE
+    # T = 0 is a no-op
+    assert lib.moe_layer_forward_fp8(ctypes.byref(_cfg(T=0)), None, None, None, None, None, None, None, 0,
+                                     None) == binding.MOE_OK
+
+
+@lib_built
+def test_fp8_workspace_is_the_dtype_layer_workspace():
+    for cfg in (configs.mixtral_decode_fp8(t) for t in configs.DECODE_TS):
+        dt = cfg.replace(weights="dtype")
+        for op in (binding.MOE_OP_GROUPED_MLP, binding.MOE_OP_LAYER):
+            assert binding.moe_workspace_size(cfg, op) == binding.moe_workspace_size(dt, op)

@@ -43,6 +43,18 @@ def test_mixtral_decode_sweep_full():
         P.check_layer_sampled(li, dev, n_tokens=T, n_experts=2, rows_per_expert=64)
 
 
+def test_mixtral_decode_fp8_sweep_full():
+    """FP8 expert weights, T in {1, 4, 16, 64}: the same codes and scales, every token checked."""
+    base = None
+    for T in configs.DECODE_TS:
+        cfg = configs.mixtral_decode_fp8(T)
+        P.say(f"case {cfg.name}")
+        li = make_inputs(cfg)
+        dev = DeviceLayer(li, threads=16, weights_from=base)
+        base = base or dev
+        P.check_layer_sampled(li, dev, n_tokens=T, n_experts=2, rows_per_expert=64)
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [configs.MIXTRAL_PREFILL, configs.QWEN3_FINE, configs.QWEN3_FINE_CF,
                                  configs.DEEPSEEK_V3], ids=lambda c: c.name)
