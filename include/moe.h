@@ -60,13 +60,25 @@ typedef enum {
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 };       /* moe_config.dtype */
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 }; /* moe_config.gating */
-enum { MOE_OP_PERMUTE = 0, MOE_OP_GROUPED_MLP = 1, MOE_OP_LAYER = 2 }; /* workspace users */
+enum { /* workspace users */
+  MOE_OP_PERMUTE = 0,
+  MOE_OP_GROUPED_MLP = 1,
+  MOE_OP_LAYER = 2,
+  MOE_OP_LAYER_BACKWARD = 3
+};
 enum { /* kernels that moe_time_next_launch can bracket */
   MOE_KERNEL_ROUTER = 0,
   MOE_KERNEL_PERMUTE_SCATTER = 1,
   MOE_KERNEL_GATE_UP = 2, /* grouped gate/up GEMM with the SiLU*mul epilogue */
   MOE_KERNEL_DOWN = 3,    /* grouped down GEMM */
-  MOE_KERNEL_COMBINE = 4
+  MOE_KERNEL_COMBINE = 4,
+  /* the grouped GEMMs of moe_layer_backward */
+  MOE_KERNEL_BWD_RECOMPUTE = 5,     /* x Wg and x Wu of every kept pair, recomputed */
+  MOE_KERNEL_BWD_DOWN_DGRAD = 6,    /* u = dy Wd */
+  MOE_KERNEL_BWD_GATE_UP_DGRAD = 7, /* dx_pair = da Wg + db Wu */
+  MOE_KERNEL_BWD_DOWN_WGRAD = 8,    /* dWd */
+  MOE_KERNEL_BWD_GATE_WGRAD = 9,    /* dWg */
+  MOE_KERNEL_BWD_UP_WGRAD = 10      /* dWu */
 };
 
 /* The problem statement of one layer (the pages' T tokens, d_model, d_ff, E experts,
@@ -228,6 +240,48 @@ MOE_API moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, c
                                  const float* router_bias, const moe_fp8_weights* experts,
                                  const moe_fp8_weights* shared, void* y, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/* Gradients written by moe_layer_backward (device pointers, layouts of the inputs they
+ * differentiate; element type cfg->dtype unless noted). */
+typedef struct moe_layer_grads {
+  void* dx;              /* [T][d] */
+  void* dw_router;       /* [E][d] */
+  float* d_router_bias;  /* [E] float; may be NULL */
+  void* dw_gate;         /* [E][f][d] */
+  void* dw_up;           /* [E][f][d] */
+  void* dw_down;         /* [E][d][f] */
+  void* dws_gate;        /* [n_shared][f_s][d]; required iff n_shared > 0 */
+  void* dws_up;          /* [n_shared][f_s][d] */
+  void* dws_down;        /* [n_shared][d][f_s] */
+  float* aux_loss;       /* [1] float: the load-balancing loss value; may be NULL */
+} moe_layer_grads;
+
+/* Backward pass of moe_layer_forward (pages: techbonafide.com "Mixture of Experts (MoE)
+ * Explained" and klaylearn.com: MoE shapes training as well as inference, and training adds
+ * auxiliary losses that keep the experts evenly loaded, after the Switch Transformer work;
+ * shipai.vats.cc "Mixture of Experts (MoE)": training adds load-balancing losses;
+ * shubhamtatvamasi.com/llm-inference/moe, "The router", "Load imbalance").
+ * Given dy [T][d], the gradient of a loss with respect to the layer output y, writes the
+ * gradients of  loss + aux_coef * E * sum_e f_e * P_e  with respect to x, the router weight
+ * and bias, every routed expert's and every shared expert's weights, where
+ *   f_e = (pairs routed to expert e before any capacity drop) / (T * k)   (a constant) and
+ *   P_e = mean over tokens of p[t][e], p the router's probability over all E experts:
+ *         softmax(logits) for MOE_SOFTMAX, s / sum(s) with s = sigmoid(logits) for MOE_SIGMOID.
+ * aux_coef = 0 leaves the balancing loss out. The expert choice and the capacity drop are
+ * piecewise constant: no gradient flows through them; dropped pairs contribute nothing.
+ * The forward is recomputed inside the call (router, permute, and x Wg, x Wu of every kept
+ * pair); the intermediates are rounded to bf16 as in the forward, products accumulate in
+ * fp32, and each gradient is rounded once to bf16 (the router's weight and input gradients
+ * accumulate in fp32 too). Experts that receive no pairs get zero gradients.
+ * cfg->dtype must be MOE_BF16 (MOE_ERR_UNSUPPORTED otherwise, and for shapes whose
+ * transposed intermediates exceed 4 GiB per matrix). Needs ws of MOE_OP_LAYER_BACKWARD
+ * bytes (it holds transposed copies of the expert weights, so it is about the size of the
+ * expert weights plus a few activation-sized buffers). T = 0 writes nothing. */
+MOE_API moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
+                              const float* router_bias, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, const void* dy, float aux_coef,
+                              const moe_layer_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
 /* Instrumentation, for measuring one kernel inside a layer call. The next launch of
  * `kernel` (MOE_KERNEL_*) made by any entry point called on THIS host thread is bracketed

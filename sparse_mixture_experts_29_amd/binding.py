@@ -21,15 +21,16 @@ LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(os.path.dirname(os.path.abs
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
-MOE_OP_PERMUTE, MOE_OP_GROUPED_MLP, MOE_OP_LAYER = 0, 1, 2
+MOE_OP_PERMUTE, MOE_OP_GROUPED_MLP, MOE_OP_LAYER, MOE_OP_LAYER_BACKWARD = 0, 1, 2, 3
 (MOE_KERNEL_ROUTER, MOE_KERNEL_PERMUTE_SCATTER, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN,
- MOE_KERNEL_COMBINE) = range(5)
+ MOE_KERNEL_COMBINE, MOE_KERNEL_BWD_RECOMPUTE, MOE_KERNEL_BWD_DOWN_DGRAD, MOE_KERNEL_BWD_GATE_UP_DGRAD,
+ MOE_KERNEL_BWD_DOWN_WGRAD, MOE_KERNEL_BWD_GATE_WGRAD, MOE_KERNEL_BWD_UP_WGRAD) = range(11)
 
 # every function the header declares
 EXPORTS = ("moe_status_string", "moe_check_config", "moe_capacity", "moe_max_kept",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_mlp", "moe_combine",
            "moe_layer_forward", "moe_expert_shard_forward", "moe_grouped_mlp_fp8",
-           "moe_layer_forward_fp8", "moe_time_next_launch")
+           "moe_layer_forward_fp8", "moe_layer_backward", "moe_time_next_launch")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -57,10 +58,19 @@ class MoeFp8Weights(ctypes.Structure):
                 ("scale_down", ctypes.c_void_p)]
 
 
+class MoeLayerGrads(ctypes.Structure):
+    """moe_layer_grads: device pointers of the gradients moe_layer_backward writes."""
+    _fields_ = [("dx", ctypes.c_void_p), ("dw_router", ctypes.c_void_p), ("d_router_bias", ctypes.c_void_p),
+                ("dw_gate", ctypes.c_void_p), ("dw_up", ctypes.c_void_p), ("dw_down", ctypes.c_void_p),
+                ("dws_gate", ctypes.c_void_p), ("dws_up", ctypes.c_void_p), ("dws_down", ctypes.c_void_p),
+                ("aux_loss", ctypes.c_void_p)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _C = ctypes.POINTER(MoeConfig)
 _F = ctypes.POINTER(MoeFp8Weights)
+_G = ctypes.POINTER(MoeLayerGrads)
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -88,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_expert_shard_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_grouped_mlp_fp8": (ctypes.c_int, [_C, _P, _P, _P, _F, _F, _P, _P, _P, sz, _P]),
         "moe_layer_forward_fp8": (ctypes.c_int, [_C, _P, _P, _P, _F, _F, _P, _P, sz, _P]),
+        "moe_layer_backward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _G, _P,
+                                              sz, _P]),
         "moe_time_next_launch": (ctypes.c_int, [ctypes.c_int, _P, _P]),
     }
     for name, (res, args) in sig.items():
@@ -228,6 +240,21 @@ def moe_layer_forward_fp8(cfg, x, w_router, router_bias, experts, shared, y, ws,
         ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias), _byref_opt(fp8_weights(experts)),
         _byref_opt(fp8_weights(shared)), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
         "moe_layer_forward_fp8")
+
+
+def layer_grads(dx, dw_router, d_router_bias, dw_gate, dw_up, dw_down, dws_gate=None, dws_up=None,
+                dws_down=None, aux_loss=None) -> MoeLayerGrads:
+    return MoeLayerGrads(_ptr(dx), _ptr(dw_router), _ptr(d_router_bias), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down),
+                         _ptr(dws_gate), _ptr(dws_up), _ptr(dws_down), _ptr(aux_loss))
+
+
+def moe_layer_backward(cfg, x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy,
+                       aux_coef: float, grads, ws, stream=None):
+    """grads: a MoeLayerGrads (see layer_grads)."""
+    _check(load_library().moe_layer_backward(
+        ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(dy), float(aux_coef), ctypes.byref(grads), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_backward")
 
 
 def moe_time_next_launch(kernel: int, begin_event, end_event) -> None:

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "router.hip", "permute.hip", "grouped_mlp.hip", "grouped_mlp_small.hip", "combine.hip"]
+SOURCES = ["api.hip", "router.hip", "permute.hip", "grouped_mlp.hip", "grouped_mlp_small.hip", "combine.hip",
+           "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -89,6 +89,106 @@ LayerWs layer_layout(const Shape& s, void* base) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
+
+// Backward workspace: the forward's routing state, the recomputed products, transposed
+// weights, the intermediates of the dgrad chain, and transposed, zero-padded activations
+// for the weight gradients, 256-byte aligned.
+struct BwdWs {
+  int32_t* idx;
+  float* gate;
+  float* logits;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_slot;
+  int32_t* pos;
+  uint8_t* drop;
+  void* permute_ws;
+  int32_t* tiles;
+  int32_t* ctrl;  // [0] m-tile count, [16, 64) counters of the six persistent GEMM launches
+  void *ab, *ab_s;                  // [rows][2f]: x Wg | x Wu
+  void *wdT, *wguT, *wdsT, *wgusT;  // [E][f][d], [E][d][2f], shared likewise
+  void *u, *u_s;                    // [rows][f]: dy Wd
+  void *dab, *dab_s, *h, *hs;       // [rows][2f]: da | db;  [rows][f]: h
+  float* d_gate;                    // [T*k]
+  void* dx_perm;                    // [max_kept][d]
+  void* dx_s;                       // [n_s + 1][T][d]: shared experts' dx, then the router's
+  float* dl;                        // [T][E]
+  float* aux_part;                  // [T]
+  int32_t* poff;                    // [E+1]
+  void *dypT, *xgT, *hT, *dabT;     // [C][np]: routed segments
+  void *dyT, *xT, *hsT, *dabsT;     // [C][tp] ([n_s][C][tp]): shared experts' token rows
+  int64_t np, tp;
+  size_t bytes;
+};
+
+BwdWs bwd_layout(const Shape& s, void* base) {
+  const uintptr_t p = reinterpret_cast<uintptr_t>(base);
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    char* r = reinterpret_cast<char*>(p + off);
+    off += align256(b);
+    return r;
+  };
+  const size_t pairs = static_cast<size_t>(s.T * s.k);
+  const size_t T = static_cast<size_t>(s.T), d = s.d, f = s.f, fs = s.f_s, E = s.E, ns = s.n_shared;
+  const size_t mk = static_cast<size_t>(s.max_kept);
+  BwdWs w;
+  w.np = round64(s.max_kept + 63 * static_cast<int64_t>(s.E));
+  w.tp = round64(s.T);
+  const size_t np = static_cast<size_t>(w.np), tp = static_cast<size_t>(w.tp);
+  w.idx = reinterpret_cast<int32_t*>(take(pairs * 4));
+  w.gate = reinterpret_cast<float*>(take(pairs * 4));
+  w.logits = reinterpret_cast<float*>(take(T * E * 4));
+  w.counts = reinterpret_cast<int32_t*>(take(E * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
+  w.sorted_slot = reinterpret_cast<int32_t*>(take(mk * 4));
+  w.pos = reinterpret_cast<int32_t*>(take(pairs * 4));
+  w.drop = reinterpret_cast<uint8_t*>(take(pairs));
+  w.permute_ws = take(permute_ws_bytes(s));
+  w.tiles = reinterpret_cast<int32_t*>(take(static_cast<size_t>(gemm_m_tile_bound(s)) * 4 * 4));
+  w.ctrl = reinterpret_cast<int32_t*>(take(64 * 4));
+  w.ab = take(mk * 2 * f * 2);
+  w.ab_s = take(ns * T * 2 * fs * 2);
+  w.wdT = take(E * f * d * 2);
+  w.wguT = take(E * d * 2 * f * 2);
+  w.wdsT = take(ns * fs * d * 2);
+  w.wgusT = take(ns * d * 2 * fs * 2);
+  w.u = take(mk * f * 2);
+  w.u_s = take(ns * T * fs * 2);
+  w.dab = take(mk * 2 * f * 2);
+  w.dab_s = take(ns * T * 2 * fs * 2);
+  w.h = take(mk * f * 2);
+  w.hs = take(ns * T * fs * 2);
+  w.d_gate = reinterpret_cast<float*>(take(pairs * 4));
+  w.dx_perm = take(mk * d * 2);
+  w.dx_s = take((ns + 1) * T * d * 2);
+  w.dl = reinterpret_cast<float*>(take(T * E * 4));
+  w.aux_part = reinterpret_cast<float*>(take(T * 4));
+  w.poff = reinterpret_cast<int32_t*>(take((E + 1) * 4));
+  w.dypT = take(d * np * 2);
+  w.xgT = take(d * np * 2);
+  w.hT = take(f * np * 2);
+  w.dabT = take(2 * f * np * 2);
+  w.dyT = take(ns ? d * tp * 2 : 0);
+  w.xT = take(ns ? d * tp * 2 : 0);
+  w.hsT = take(ns * fs * tp * 2);
+  w.dabsT = take(ns * 2 * fs * tp * 2);
+  w.bytes = off;
+  return w;
+}
+
+// every matrix a kernel addresses with 32-bit byte offsets stays under 4 GiB
+bool bwd_fits_32bit(const Shape& s) {
+  const int64_t lim = int64_t{1} << 32;
+  const int64_t np = round64(s.max_kept + 63 * static_cast<int64_t>(s.E)), tp = round64(s.T);
+  const int64_t wide = std::max<int64_t>(s.d, 2 * static_cast<int64_t>(s.f));
+  const int64_t wide_s = std::max<int64_t>(s.d, 2 * static_cast<int64_t>(s.f_s));
+  return np * wide * 2 < lim && tp * wide_s * 2 < lim && s.T * static_cast<int64_t>(s.d) * 2 < lim &&
+         s.max_kept * 2 * static_cast<int64_t>(s.f) * 2 < lim &&
+         static_cast<int64_t>(s.n_shared) * s.T * 2 * s.f_s * 2 < lim;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // FP8 weights: every member present and 16-byte aligned (the kernels read 16-byte vectors
@@ -176,6 +276,10 @@ moe_status moe_workspace_size(const moe_config* cfg, int op, size_t* bytes) {
     case MOE_OP_PERMUTE: *bytes = permute_ws_bytes(s); break;
     case MOE_OP_GROUPED_MLP: *bytes = grouped_ws_bytes(s); break;
     case MOE_OP_LAYER: *bytes = layer_layout(s, nullptr).bytes; break;
+    case MOE_OP_LAYER_BACKWARD:
+      if (s.dtype != MOE_BF16 || !bwd_fits_32bit(s)) return MOE_ERR_UNSUPPORTED;
+      *bytes = bwd_layout(s, nullptr).bytes;
+      break;
     default: return MOE_ERR_INVALID_ARG;
   }
   return MOE_OK;
@@ -358,13 +462,223 @@ moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, const voi
   return hip_status(e);
 }
 
+moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
+                              const float* router_bias, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, const void* dy, float aux_coef,
+                              const moe_layer_grads* g, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status r = to_shape(cfg, &s);
+  if (r != MOE_OK) return r;
+  if (!std::isfinite(aux_coef)) return MOE_ERR_INVALID_ARG;
+  if (s.dtype != MOE_BF16 || !bwd_fits_32bit(s)) return MOE_ERR_UNSUPPORTED;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !dy || !g || !ws) return MOE_ERR_INVALID_ARG;
+  if (!g->dx || !g->dw_router || !g->dw_gate || !g->dw_up || !g->dw_down) return MOE_ERR_INVALID_ARG;
+  if (s.n_shared > 0 && (!ws_gate || !ws_up || !ws_down || !g->dws_gate || !g->dws_up || !g->dws_down))
+    return MOE_ERR_INVALID_ARG;
+  BwdWs w = bwd_layout(s, ws);
+  if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int d = s.d, f = s.f, fs = s.f_s, E = s.E, ns = s.n_shared;
+  const int T = static_cast<int>(s.T);
+  hipError_t e = launch_fill_u32(w.ctrl, 64, 0, st);
+  // forward state: routing, permutation, tile table
+  if (e == hipSuccess) e = launch_route(s, x, w_router, router_bias, w.idx, w.gate, w.logits, st);
+  if (e == hipSuccess)
+    e = launch_permute(s, w.idx, w.counts, w.offsets, w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
+  if (e == hipSuccess) e = launch_build_tiles(s, w.offsets, w.tiles, w.ctrl, w.ctrl + 16, st);
+  // transposed weights: Wd^T [E][f][d] and (Wg | Wu)^T [E][d][2f]
+  if (e == hipSuccess) e = launch_transpose_batched(w_down, d, f, int64_t{d} * f, w.wdT, d, 0, int64_t{f} * d, E, st);
+  if (e == hipSuccess)
+    e = launch_transpose_batched(w_gate, f, d, int64_t{f} * d, w.wguT, 2 * f, 0, int64_t{d} * 2 * f, E, st);
+  if (e == hipSuccess)
+    e = launch_transpose_batched(w_up, f, d, int64_t{f} * d, w.wguT, 2 * f, f, int64_t{d} * 2 * f, E, st);
+  if (ns > 0) {
+    if (e == hipSuccess)
+      e = launch_transpose_batched(ws_down, d, fs, int64_t{d} * fs, w.wdsT, d, 0, int64_t{fs} * d, ns, st);
+    if (e == hipSuccess)
+      e = launch_transpose_batched(ws_gate, fs, d, int64_t{fs} * d, w.wgusT, 2 * fs, 0, int64_t{d} * 2 * fs, ns, st);
+    if (e == hipSuccess)
+      e = launch_transpose_batched(ws_up, fs, d, int64_t{fs} * d, w.wgusT, 2 * fs, fs, int64_t{d} * 2 * fs, ns, st);
+  }
+  GemmLaunch L{};
+  L.tiles = w.tiles;
+  L.n_tiles = w.ctrl;
+  L.m_bound = gemm_m_tile_bound(s);
+  L.E = E;
+  L.k = s.k;
+  L.T = T;
+  L.n_shared = ns;
+  L.sorted_slot = w.sorted_slot;
+  // (1) recompute a = x Wg and b = x Wu for every kept pair and shared row
+  L.mode = kGemmGatedSave;
+  L.in_r = L.in_s = x;
+  L.w0_r = w_gate;
+  L.w1_r = w_up;
+  L.w0_s = ws_gate;
+  L.w1_s = ws_up;
+  L.out_r = w.ab;
+  L.out_s = w.ab_s;
+  L.N_r = f;
+  L.K_r = d;
+  L.N_s = fs;
+  L.K_s = d;
+  L.queue = w.ctrl + 16;
+  if (e == hipSuccess) {
+    timing_begin(MOE_KERNEL_BWD_RECOMPUTE, st);
+    e = launch_grouped_gemm(L, st);
+    timing_end(MOE_KERNEL_BWD_RECOMPUTE, st);
+  }
+  // (2) u = dy Wd: the pair's token row of dy against Wd^T
+  L.mode = kGemmPlainGather;
+  L.in_r = L.in_s = dy;
+  L.w0_r = w.wdT;
+  L.w1_r = nullptr;
+  L.w0_s = w.wdsT;
+  L.w1_s = nullptr;
+  L.out_r = w.u;
+  L.out_s = w.u_s;
+  L.queue = w.ctrl + 24;
+  if (e == hipSuccess) {
+    timing_begin(MOE_KERNEL_BWD_DOWN_DGRAD, st);
+    e = launch_grouped_gemm(L, st);
+    timing_end(MOE_KERNEL_BWD_DOWN_DGRAD, st);
+  }
+  // (3) SwiGLU backward: da | db, h, and each pair's gate gradient u . h
+  if (e == hipSuccess) e = launch_fill_u32(w.d_gate, s.T * s.k, 0, st);
+  if (e == hipSuccess)
+    e = launch_swiglu_bwd(s, w.ab, w.u, w.ab_s, w.u_s, w.offsets, w.sorted_slot, w.gate, w.dab, w.h, w.dab_s, w.hs,
+                          w.d_gate, st);
+  // (4) dx of every pair: (da | db) against (Wg | Wu)^T
+  L.mode = kGemmPlain;
+  L.sorted_slot = nullptr;
+  L.in_r = w.dab;
+  L.in_s = w.dab_s;
+  L.w0_r = w.wguT;
+  L.w0_s = w.wgusT;
+  L.out_r = w.dx_perm;
+  L.out_s = w.dx_s;
+  L.N_r = d;
+  L.K_r = 2 * f;
+  L.N_s = d;
+  L.K_s = 2 * fs;
+  L.queue = w.ctrl + 32;
+  if (e == hipSuccess) {
+    timing_begin(MOE_KERNEL_BWD_GATE_UP_DGRAD, st);
+    e = launch_grouped_gemm(L, st);
+    timing_end(MOE_KERNEL_BWD_GATE_UP_DGRAD, st);
+  }
+  // (5) router: logit gradients (+ balancing loss), weight, bias and input gradients
+  void* dx_router = static_cast<char*>(w.dx_s) + static_cast<size_t>(ns) * s.T * d * 2;
+  if (e == hipSuccess)
+    e = launch_router_bwd(s, w.logits, w.idx, w.gate, w.d_gate, w.counts, aux_coef, w.dl, w.aux_part, g->aux_loss,
+                          g->d_router_bias, st);
+  if (e == hipSuccess) e = launch_fma_gemm(w.dl, 1, E, x, d, E, d, s.T, g->dw_router, d, st);
+  if (e == hipSuccess) e = launch_fma_gemm(w.dl, E, 1, w_router, d, s.T, d, E, dx_router, d, st);
+  // (6) dx = every kept pair's dx + shared experts' + router's (a combine with unit gates)
+  if (e == hipSuccess) {
+    Shape s2 = s;
+    s2.n_shared = ns + 1;
+    e = launch_combine(s2, w.dx_perm, w.pos, nullptr, w.dx_s, g->dx, st);
+  }
+  // (7) weight gradients over transposed, zero-padded per-expert segments
+  if (e == hipSuccess) e = launch_pad_offsets(w.offsets, E, w.poff, st);
+  const int np = static_cast<int>(w.np), tp = static_cast<int>(w.tp);
+  if (e == hipSuccess)
+    e = launch_transpose_segments(dy, d, 0, w.offsets, w.poff, E, 0, w.np, w.sorted_slot, s.k, w.gate, d, w.dypT, np,
+                                  0, 1, st);
+  if (e == hipSuccess)
+    e = launch_transpose_segments(x, d, 0, w.offsets, w.poff, E, 0, w.np, w.sorted_slot, s.k, nullptr, d, w.xgT, np, 0,
+                                  1, st);
+  if (e == hipSuccess)
+    e = launch_transpose_segments(w.h, f, 0, w.offsets, w.poff, E, 0, w.np, nullptr, s.k, nullptr, f, w.hT, np, 0, 1,
+                                  st);
+  if (e == hipSuccess)
+    e = launch_transpose_segments(w.dab, 2 * f, 0, w.offsets, w.poff, E, 0, w.np, nullptr, s.k, nullptr, 2 * f, w.dabT,
+                                  np, 0, 1, st);
+  if (ns > 0) {
+    if (e == hipSuccess)
+      e = launch_transpose_segments(dy, d, 0, nullptr, nullptr, 1, T, w.tp, nullptr, s.k, nullptr, d, w.dyT, tp, 0, 1,
+                                    st);
+    if (e == hipSuccess)
+      e = launch_transpose_segments(x, d, 0, nullptr, nullptr, 1, T, w.tp, nullptr, s.k, nullptr, d, w.xT, tp, 0, 1,
+                                    st);
+    if (e == hipSuccess)
+      e = launch_transpose_segments(w.hs, fs, int64_t{T} * fs, nullptr, nullptr, 1, T, w.tp, nullptr, s.k, nullptr, fs,
+                                    w.hsT, tp, int64_t{fs} * tp, ns, st);
+    if (e == hipSuccess)
+      e = launch_transpose_segments(w.dab_s, 2 * fs, int64_t{T} * 2 * fs, nullptr, nullptr, 1, T, w.tp, nullptr, s.k,
+                                    nullptr, 2 * fs, w.dabsT, tp, int64_t{2} * fs * tp, ns, st);
+  }
+  L = GemmLaunch{};
+  L.mode = kGemmWgrad;
+  L.E = E;
+  L.k = s.k;
+  L.T = T;
+  L.n_shared = ns;
+  L.koff = w.poff;
+  L.ld_in_r = L.ld_w_r = np;
+  L.ld_in_s = L.ld_w_s = tp;
+  L.K_s = tp;
+  // dWd[e] [d][f] = sum over the segment of (g dy)^T h
+  L.in_r = w.dypT;
+  L.w0_r = w.hT;
+  L.in_s = w.dyT;
+  L.in_s_gstride = 0;
+  L.w0_s = w.hsT;
+  L.w_s_gstride = int64_t{fs} * tp;
+  L.M_r = d;
+  L.N_r = f;
+  L.M_s = d;
+  L.N_s = fs;
+  L.out_r = g->dw_down;
+  L.out_s = g->dws_down;
+  L.queue = w.ctrl + 40;
+  if (e == hipSuccess) {
+    timing_begin(MOE_KERNEL_BWD_DOWN_WGRAD, st);
+    e = launch_grouped_gemm(L, st);
+    timing_end(MOE_KERNEL_BWD_DOWN_WGRAD, st);
+  }
+  // dWg[e] [f][d] = da^T x, dWu[e] = db^T x
+  L.in_r = w.dabT;
+  L.w0_r = w.xgT;
+  L.in_s = w.dabsT;
+  L.in_s_gstride = int64_t{2} * fs * tp;
+  L.w0_s = w.xT;
+  L.w_s_gstride = 0;
+  L.M_r = f;
+  L.N_r = d;
+  L.M_s = fs;
+  L.N_s = d;
+  L.out_r = g->dw_gate;
+  L.out_s = g->dws_gate;
+  L.queue = w.ctrl + 48;
+  if (e == hipSuccess) {
+    timing_begin(MOE_KERNEL_BWD_GATE_WGRAD, st);
+    e = launch_grouped_gemm(L, st);
+    timing_end(MOE_KERNEL_BWD_GATE_WGRAD, st);
+  }
+  L.in_r = static_cast<const char*>(w.dabT) + static_cast<size_t>(f) * np * 2;
+  L.in_s = static_cast<const char*>(w.dabsT) + static_cast<size_t>(fs) * tp * 2;
+  L.out_r = g->dw_up;
+  L.out_s = g->dws_up;
+  L.queue = w.ctrl + 56;
+  if (e == hipSuccess) {
+    timing_begin(MOE_KERNEL_BWD_UP_WGRAD, st);
+    e = launch_grouped_gemm(L, st);
+    timing_end(MOE_KERNEL_BWD_UP_WGRAD, st);
+  }
+  return hip_status(e);
+}
+
 moe_status moe_time_next_launch(int kernel, void* begin_event, void* end_event) {
   TimingRequest& r = timing_request();
   if (kernel == -1) {
     r.kernel = -1;
     return MOE_OK;
   }
-  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_COMBINE || !begin_event || !end_event)
+  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_BWD_UP_WGRAD || !begin_event || !end_event)
     return MOE_ERR_INVALID_ARG;
   r.kernel = kernel;
   r.begin = static_cast<hipEvent_t>(begin_event);

@@ -60,6 +60,45 @@ constexpr int kSmallMMaxRows = 64;
 bool use_small_m(const Shape& s);
 int small_m_splits(const Shape& s, bool gated);
 size_t small_m_ws_bytes(const Shape& s);
+// Launches of the bf16 grouped GEMM (grouped_mlp.hip): out[row][n] = sum_k in[src(row)][k] *
+// w_g[n][k] over tiles of 256 rows x 256 weight rows.
+enum GemmMode {
+  kGemmGated = 0,        // forward gate/up with the SiLU*mul epilogue: h [rows][N]
+  kGemmPlain = 1,        // forward down: routed rows read in[row], shared rows in[s*T + t]
+  kGemmGatedSave = 2,    // gate/up storing both products, [rows][2N] = (x Wg | x Wu)
+  kGemmPlainGather = 3,  // one weight matrix, rows read as the gated launch reads them
+  kGemmWgrad = 4         // weight gradients: fixed M rows per group, K = the group's segment
+};
+struct GemmLaunch {
+  int mode;
+  const void* in_r;             // routed input
+  const void* in_s;             // shared input
+  const int32_t* sorted_slot;   // gather of the gated / gather modes
+  const int32_t* tiles;         // device tile table (not kGemmWgrad)
+  const int32_t* n_tiles;       // device m-tile count (not kGemmWgrad)
+  int64_t m_bound;              // bound on m-tiles (grid size)
+  const void* w0_r;
+  const void* w1_r;
+  const void* w0_s;
+  const void* w1_s;
+  void* out_r;
+  void* out_s;
+  int N_r, K_r, N_s, K_s;
+  int E, k, T, n_shared;
+  int32_t* queue;               // 8 zeroed counters
+  // kGemmWgrad
+  const int32_t* koff;
+  int ld_in_r, ld_w_r, ld_in_s, ld_w_s;
+  int64_t in_s_gstride, w_s_gstride;
+  int M_r, M_s;
+};
+hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st);
+// the device tile table of the grouped GEMM (routed groups from offsets, then shared); also
+// zeroes 16 queue counters
+hipError_t launch_build_tiles(const Shape& s, const int32_t* offsets, int32_t* tiles, int32_t* n_tiles,
+                              int32_t* queues, hipStream_t st);
+int64_t gemm_m_tile_bound(const Shape& s);
+
 // FP8 (E4M3) expert weights: per-output-row scales of the routed experts, [E][f] (gate, up)
 // and [E][d] (down), and of the shared experts, [n_s][f_s] and [n_s][d]; gate null for
 // weights in the layer's dtype.
@@ -103,6 +142,24 @@ hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos
                           const float* gate, const void* y_shared, void* y, hipStream_t st);
 
 // Per-host-thread request of moe_time_next_launch.
+// Backward pass (backward.hip).
+hipError_t launch_transpose_batched(const void* src, int R, int C, int64_t src_bstride, void* dst, int ldd, int coff,
+                                    int64_t dst_bstride, int batch, hipStream_t st);
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
+hipError_t launch_transpose_segments(const void* src, int src_ld, int64_t src_bstride, const int32_t* off,
+                                     const int32_t* poff, int nseg, int len1, int64_t padded_rows_bound,
+                                     const int32_t* sorted_slot, int k, const float* gate, int C, void* dst, int ldd,
+                                     int64_t dst_bstride, int batch, hipStream_t st);
+hipError_t launch_swiglu_bwd(const Shape& s, const void* ab, const void* u, const void* ab_s, const void* u_s,
+                             const int32_t* offsets, const int32_t* sorted_slot, const float* gate, void* dab, void* h,
+                             void* dab_s, void* hs, float* d_gate, hipStream_t st);
+hipError_t launch_router_bwd(const Shape& s, const float* logits, const int32_t* idx, const float* gate,
+                             const float* d_gate, const int32_t* counts, float aux_coef, float* dl, float* aux_part,
+                             float* aux_loss, float* d_bias, hipStream_t st);
+hipError_t launch_fma_gemm(const float* A, int64_t sam, int64_t sak, const void* B, int64_t ldb, int64_t M, int N,
+                           int64_t K, void* C, int64_t ldc, hipStream_t st);
+hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st);
+
 struct TimingRequest {
   int kernel = -1;
   hipEvent_t begin = nullptr, end = nullptr;

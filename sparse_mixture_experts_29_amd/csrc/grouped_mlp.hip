@@ -67,6 +67,14 @@ struct GemmArgs {
   int E, k, T;
   int n_tiles_n;               // n-tiles of the widest group
   int32_t* queue;              // [8] per-XCD tile counters, zeroed by build_tiles_kernel
+  // weight-gradient launches (kGemmWgrad): the token operand is a transposed activation
+  // [M][ld_in], the weight operand a transposed activation [N][ld_w], and a group's K range
+  // is its padded segment of the columns
+  const int32_t* koff;         // [E+1] first column of each routed group's segment
+  int ld_in_r, ld_w_r, ld_in_s, ld_w_s;
+  int64_t in_s_gstride, w_s_gstride;  // elements between consecutive shared groups
+  int M_r, M_s;                // output rows of a routed / shared group
+  int mt_r, mt_s, n_m;         // m-tiles of a routed / shared group, and in all
 };
 
 // Chunk swizzle of LDS row r (its 16-byte chunk c is stored at slot c ^ swz(r)). It makes
@@ -280,7 +288,7 @@ static_assert(IPW == 8 || BK != 32, "the pipelined loop issues 8 DMA instruction
 // K loop and epilogue of one wave, for LIVE (compile-time) token sub-tiles of 32 rows that
 // hold data. Every wave of a block runs the same number of K steps and barriers; waves
 // with fewer live sub-tiles skip MFMAs, not loads.
-template <bool GATED, int BT, int LIVE>
+template <bool GATED, int BT, int LIVE, bool SAVE = false>
 __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K, int wave,
                                           int lane, int row0, int row1, int n0, int N,
                                           bf16_t* out, int64_t out_row_base) {
@@ -370,8 +378,25 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
   for (int j = 0; j < LIVE; ++j) {
     const int row = row0 + tok0 + j * 32 + l32;
     if (row >= row1) continue;
-    bf16_t* op = out + (out_row_base + row) * N;
-    if (GATED) {
+    // SAVE: the gate and up products themselves, side by side in a row of 2N
+    bf16_t* op = out + (out_row_base + row) * (SAVE ? 2 * N : N);
+    if (GATED && SAVE) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * 64 + i * 32 + q * 8 + khalf * 4;
+          if (n < N) {
+            uint2 pa, pb;
+            pa.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+            pa.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+            pb.x = pack_bf16x2(acc[i + 2][j][q * 4 + 0], acc[i + 2][j][q * 4 + 1]);
+            pb.y = pack_bf16x2(acc[i + 2][j][q * 4 + 2], acc[i + 2][j][q * 4 + 3]);
+            *reinterpret_cast<uint2*>(op + n) = pa;
+            *reinterpret_cast<uint2*>(op + N + n) = pb;
+          }
+        }
+    } else if (GATED) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -412,8 +437,16 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
 // wave 128 weight rows x BT/2 tokens of v_mfma_f32_32x32x16_bf16 accumulators. L is the
 // tile's index in raster order: groups of kGroupM m-tiles sweep every n-tile, so a weight
 // tile is read by kGroupM m-tiles close together in time.
-template <bool GATED, int BT>
+// MODE (GemmMode): the forward launches (gated with the SiLU*mul epilogue; plain), the
+// gated launch storing both products (kGemmGatedSave), a plain launch whose routed rows
+// gather the input by sorted_slot as the gated launch does (kGemmPlainGather), and the
+// weight-gradient launch (kGemmWgrad, fixed M rows per group, K = the group's segment).
+template <int MODE, int BT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L, int n_m, int n_n) {
+  constexpr bool GATED = MODE == kGemmGated || MODE == kGemmGatedSave;
+  constexpr bool SAVE = MODE == kGemmGatedSave;
+  constexpr bool GATHER = GATED || MODE == kGemmPlainGather;
+  constexpr bool WGRAD = MODE == kGemmWgrad;
   constexpr int WT = BT / 2;  // token rows per wave
   constexpr int TJ = WT / 32; // token sub-tiles per wave
   const int in_group = kGroupM * n_n;
@@ -423,19 +456,63 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
   const int n_tile = (L % in_group) / gsz;
 
   // tile bookkeeping is wave-uniform: keep it in scalar registers
-  const int g = __builtin_amdgcn_readfirstlane(a.tiles[m_idx * kTileEntries + 0]);
-  const int row0 = __builtin_amdgcn_readfirstlane(a.tiles[m_idx * kTileEntries + 1]);
-  const int row1 = __builtin_amdgcn_readfirstlane(a.tiles[m_idx * kTileEntries + 2]);
+  int g, row0, row1;
+  if constexpr (WGRAD) {
+    const int routed_m = a.E * a.mt_r;
+    if (m_idx < routed_m) {
+      g = m_idx / a.mt_r;
+      row0 = (m_idx % a.mt_r) * BT;
+      row1 = min(row0 + BT, a.M_r);
+    } else {
+      g = a.E + (m_idx - routed_m) / a.mt_s;
+      row0 = ((m_idx - routed_m) % a.mt_s) * BT;
+      row1 = min(row0 + BT, a.M_s);
+    }
+    g = __builtin_amdgcn_readfirstlane(g);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    row1 = __builtin_amdgcn_readfirstlane(row1);
+  } else {
+    g = __builtin_amdgcn_readfirstlane(a.tiles[m_idx * kTileEntries + 0]);
+    row0 = __builtin_amdgcn_readfirstlane(a.tiles[m_idx * kTileEntries + 1]);
+    row1 = __builtin_amdgcn_readfirstlane(a.tiles[m_idx * kTileEntries + 2]);
+  }
   const bool shared = g >= a.E;
   const int N = shared ? a.N_s : a.N_r;
-  const int K = shared ? a.K_s : a.K_r;
   constexpr int BNO = GATED ? BW / 2 : BW;  // output columns per tile
   const int n0 = n_tile * BNO;
   if (n0 >= N) return;
   const int gi = shared ? g - a.E : g;
-  const bf16_t* w0 = (shared ? a.w0_s : a.w0_r) + static_cast<int64_t>(gi) * N * K;
-  const bf16_t* w1 = GATED ? (shared ? a.w1_s : a.w1_r) + static_cast<int64_t>(gi) * N * K : nullptr;
-  const bf16_t* in = shared ? a.in_s : a.in_r;
+  int K, ldw, ldin;
+  const bf16_t* w0;
+  const bf16_t* w1 = nullptr;
+  const bf16_t* in;
+  if constexpr (WGRAD) {
+    // opaque copies: a select between two of these kernel-argument fields is otherwise
+    // folded into an indexed access of a scratch copy of the arguments
+    int lw_r = a.ld_w_r, lw_s = a.ld_w_s, li_r = a.ld_in_r, li_s = a.ld_in_s;
+    asm volatile("" : "+s"(lw_r), "+s"(lw_s), "+s"(li_r), "+s"(li_s));
+    if (shared) {
+      K = a.K_s;
+      w0 = a.w0_s + gi * a.w_s_gstride;
+      in = a.in_s + gi * a.in_s_gstride;
+      ldw = lw_s;
+      ldin = li_s;
+    } else {
+      const int k0 = __builtin_amdgcn_readfirstlane(a.koff[g]);
+      K = __builtin_amdgcn_readfirstlane(a.koff[g + 1]) - k0;
+      w0 = a.w0_r + k0;
+      in = a.in_r + k0;
+      ldw = lw_r;
+      ldin = li_r;
+    }
+  } else {
+    K = shared ? a.K_s : a.K_r;
+    w0 = (shared ? a.w0_s : a.w0_r) + static_cast<int64_t>(gi) * N * K;
+    if (GATED) w1 = (shared ? a.w1_s : a.w1_r) + static_cast<int64_t>(gi) * N * K;
+    in = shared ? a.in_s : a.in_r;
+    ldw = K;
+    ldin = K;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -454,7 +531,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
       const int r = i * RPI + lrow;  // row within the wave's 128 (row mod 128 fixes the swizzle)
       const int n = min(nbase + r, N - 1);
       const int c = (lane % CH) ^ swz(r);
-      dp.off[i] = static_cast<uint32_t>(n) * static_cast<uint32_t>(K) * 2u + (c << 4);
+      dp.off[i] = static_cast<uint32_t>(n) * static_cast<uint32_t>(ldw) * 2u + (c << 4);
     }
   } else {
     dp.base = reinterpret_cast<const char*>(in);
@@ -464,30 +541,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
       int r = row0 + tr;
       r = r < row1 ? r : row0;
       int64_t src;
-      if (shared)
-        src = GATED ? r : static_cast<int64_t>(gi) * a.T + r;
+      if (WGRAD)
+        src = r;
+      else if (shared)
+        src = GATHER ? r : static_cast<int64_t>(gi) * a.T + r;
       else
-        src = GATED ? a.sorted_slot[r] / a.k : r;
+        src = GATHER ? a.sorted_slot[r] / a.k : r;
       const int c = (lane % CH) ^ swz(BW + tr);
-      dp.off[i] = static_cast<uint32_t>(src * K * 2 + (c << 4));
+      dp.off[i] = static_cast<uint32_t>(src * ldin * 2 + (c << 4));
     }
   }
 
   bf16_t* out = shared ? a.out_s : a.out_r;
-  const int64_t out_row_base = shared ? static_cast<int64_t>(gi) * a.T : 0;
+  int64_t out_row_base;
+  if constexpr (WGRAD)
+    out_row_base = static_cast<int64_t>(gi) * (shared ? a.M_s : a.M_r);
+  else
+    out_row_base = shared ? static_cast<int64_t>(gi) * a.T : 0;
   const int valid_rows = row1 - row0 - (wave >> 1) * WT;
   const int live = __builtin_amdgcn_readfirstlane(valid_rows <= 0 ? 0 : min(TJ, (valid_rows + 31) / 32));
   static_assert(TJ == 4 || TJ == 2, "token sub-tiles per wave");
   if (live >= TJ)
-    tile_loop<GATED, BT, TJ>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, TJ, SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (live == 0)
-    tile_loop<GATED, BT, 0>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, 0, SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (live == 1)
-    tile_loop<GATED, BT, 1>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, 1, SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (TJ == 4 && live == 2)
-    tile_loop<GATED, BT, (TJ == 4 ? 2 : 1)>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, (TJ == 4 ? 2 : 1), SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else
-    tile_loop<GATED, BT, (TJ == 4 ? 3 : 1)>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, (TJ == 4 ? 3 : 1), SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
 }
 
 // Persistent launch: one block per CU takes tiles from queues until all are done. The
@@ -495,7 +578,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
 // L2), and a block first drains the range of the XCD it runs on, then helps the others,
 // so the CUs finish together however unequal the tiles are (ragged tiles cost less).
 // Every block leaves once every counter is past its range.
-template <bool GATED, int BT>
+template <int MODE, int BT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
   // one LDS object (a second one costs a full DMA drain per stage: the compiler's wait
   // insertion then cannot tell the DMA targets from the operand reads); the tile index
@@ -503,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
   constexpr int kRing = NST * (BW + BT) * BK;
   __shared__ __attribute__((aligned(1024))) bf16_t lds[kRing + 64];
   int* next_tile = reinterpret_cast<int*>(lds + kRing);
-  const int n_m = *a.n_tiles;
+  const int n_m = MODE == kGemmWgrad ? a.n_m : *a.n_tiles;
   const int n_n = a.n_tiles_n;
   const int G = n_m * n_n;
   const int per_xcd = (G + 7) / 8;
@@ -525,7 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
     const int L = __builtin_amdgcn_readfirstlane(*next_tile);
     __syncthreads();  // every wave has read next_tile before it is written again
     if (L < 0) return;
-    gemm_tile<GATED, BT>(a, lds, L, n_m, n_n);
+    gemm_tile<MODE, BT>(a, lds, L, n_m, n_n);
   }
 }
 
@@ -728,6 +811,69 @@ int cu_count() {
   return cached[dev];
 }
 
+int64_t gemm_m_tile_bound(const Shape& s) { return m_tile_bound(s); }
+
+hipError_t launch_build_tiles(const Shape& s, const int32_t* offsets, int32_t* tiles, int32_t* n_tiles,
+                              int32_t* queues, hipStream_t st) {
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, s.E, s.n_shared,
+                     static_cast<int>(s.T), tile_rows(s), tiles, n_tiles, queues);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st) {
+  GemmArgs a{};
+  a.in_r = static_cast<const bf16_t*>(L.in_r);
+  a.in_s = static_cast<const bf16_t*>(L.in_s);
+  a.sorted_slot = L.sorted_slot;
+  a.tiles = L.tiles;
+  a.n_tiles = L.n_tiles;
+  a.w0_r = static_cast<const bf16_t*>(L.w0_r);
+  a.w1_r = static_cast<const bf16_t*>(L.w1_r);
+  a.w0_s = static_cast<const bf16_t*>(L.w0_s);
+  a.w1_s = static_cast<const bf16_t*>(L.w1_s);
+  a.out_r = static_cast<bf16_t*>(L.out_r);
+  a.out_s = static_cast<bf16_t*>(L.out_s);
+  a.N_r = L.N_r;
+  a.K_r = L.K_r;
+  a.N_s = L.N_s;
+  a.K_s = L.K_s;
+  a.E = L.E;
+  a.k = L.k;
+  a.T = L.T;
+  a.queue = L.queue;
+  a.koff = L.koff;
+  a.ld_in_r = L.ld_in_r;
+  a.ld_w_r = L.ld_w_r;
+  a.ld_in_s = L.ld_in_s;
+  a.ld_w_s = L.ld_w_s;
+  a.in_s_gstride = L.in_s_gstride;
+  a.w_s_gstride = L.w_s_gstride;
+  a.M_r = L.M_r;
+  a.M_s = L.M_s;
+  const bool gated = L.mode == kGemmGated || L.mode == kGemmGatedSave;
+  const int n_max = L.n_shared > 0 && L.N_s > L.N_r ? L.N_s : L.N_r;
+  a.n_tiles_n = gated ? (n_max + BW / 2 - 1) / (BW / 2) : (n_max + BW - 1) / BW;
+  int64_t mb = L.m_bound;
+  if (L.mode == kGemmWgrad) {
+    a.mt_r = (L.M_r + kBT - 1) / kBT;
+    a.mt_s = L.n_shared > 0 ? (L.M_s + kBT - 1) / kBT : 1;
+    a.n_m = L.E * a.mt_r + L.n_shared * (L.n_shared > 0 ? a.mt_s : 0);
+    mb = a.n_m;
+  }
+  const int64_t grid = std::min<int64_t>(cu_count(), static_cast<int64_t>(a.n_tiles_n) * mb);
+  if (grid <= 0) return hipSuccess;
+  const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
+  switch (L.mode) {
+    case kGemmGated: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGated, kBT>), gd, bd, 0, st, a); break;
+    case kGemmPlain: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kBT>), gd, bd, 0, st, a); break;
+    case kGemmGatedSave: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGatedSave, kBT>), gd, bd, 0, st, a); break;
+    case kGemmPlainGather: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainGather, kBT>), gd, bd, 0, st, a); break;
+    case kGemmWgrad: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmWgrad, kBT>), gd, bd, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sorted_slot,
                               const int32_t* offsets, const void* wg, const void* wu,
                               const void* wd, const void* swg, const void* swu, const void* swd,
@@ -770,7 +916,7 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     const int n_cu = cu_count();
     const int64_t g1 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb);
     timing_begin(MOE_KERNEL_GATE_UP, st);
-    hipLaunchKernelGGL((grouped_gemm_bf16<true, kBT>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGated, kBT>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0, st, a);
     timing_end(MOE_KERNEL_GATE_UP, st);
     // launch 2: y = h Wd
     a.sorted_slot = nullptr;
@@ -790,7 +936,7 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.queue = queues + 8;
     const int64_t g2 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb);
     timing_begin(MOE_KERNEL_DOWN, st);
-    hipLaunchKernelGGL((grouped_gemm_bf16<false, kBT>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kBT>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, st, a);
     timing_end(MOE_KERNEL_DOWN, st);
   } else {
     GemmArgsF32 a{};

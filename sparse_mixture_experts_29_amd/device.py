@@ -108,6 +108,15 @@ class DeviceLayer:
                                   self.y, self.ws, stream)
         return self.y
 
+    def backward(self, dy: torch.Tensor, aux_coef: float = 0.0, grads: Optional["LayerGrads"] = None,
+                 stream=None) -> "LayerGrads":
+        """moe_layer_backward for the output gradient dy [T][d]; returns the gradient buffers."""
+        g = grads if grads is not None else LayerGrads(self)
+        binding.moe_layer_backward(self.cfg, self.x, self.w_router, self.router_bias, self.w_gate, self.w_up,
+                                   self.w_down, self.ws_gate, self.ws_up, self.ws_down, dy, aux_coef, g.struct, g.ws,
+                                   stream)
+        return g
+
     # ---------------------------------------------------------------- step by step
     def stage_buffers(self) -> dict:
         cfg, dev = self.cfg, self.device
@@ -154,6 +163,33 @@ class DeviceLayer:
 
     def combine(self, b: dict, stream=None):
         binding.moe_combine(self.cfg, b["y_perm"], b["pos"], b["gate"], b["y_shared"], b["y"], stream)
+
+
+class LayerGrads:
+    """Device buffers for the gradients of a DeviceLayer (moe_layer_backward) and the
+    backward workspace."""
+
+    def __init__(self, layer: "DeviceLayer"):
+        cfg, dev = layer.cfg, layer.device
+        dt = torch_dtype(cfg)
+        E, d, f = cfg.n_experts, cfg.d_model, cfg.d_ff
+        self.dx = torch.empty((cfg.T, d), dtype=dt, device=dev)
+        self.dw_router = torch.empty((E, d), dtype=dt, device=dev)
+        self.d_router_bias = torch.empty(E, dtype=torch.float32, device=dev)
+        self.dw_gate = torch.empty((E, f, d), dtype=dt, device=dev)
+        self.dw_up = torch.empty((E, f, d), dtype=dt, device=dev)
+        self.dw_down = torch.empty((E, d, f), dtype=dt, device=dev)
+        self.dws_gate = self.dws_up = self.dws_down = None
+        if cfg.n_shared:
+            fs = cfg.d_ff_shared
+            self.dws_gate = torch.empty((cfg.n_shared, fs, d), dtype=dt, device=dev)
+            self.dws_up = torch.empty((cfg.n_shared, fs, d), dtype=dt, device=dev)
+            self.dws_down = torch.empty((cfg.n_shared, d, fs), dtype=dt, device=dev)
+        self.aux_loss = torch.empty(1, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(binding.moe_workspace_size(cfg, binding.MOE_OP_LAYER_BACKWARD), dtype=torch.uint8,
+                              device=dev)
+        self.struct = binding.layer_grads(self.dx, self.dw_router, self.d_router_bias, self.dw_gate, self.dw_up,
+                                          self.dw_down, self.dws_gate, self.dws_up, self.dws_down, self.aux_loss)
 
 
 def _upload_fp8(li: LayerInputs, n: int, f: int, d: int, device, threads: int, shared: bool):

@@ -12,6 +12,7 @@ so that experts can be produced one at a time and regenerated on demand):
   (std = 1/sqrt(fan_in));
 * router bias: none; "zipf" = a seeded permutation gives each expert a rank r in 1..E,
   w = r^-s, and the bias is w min-max scaled linearly onto [-2, 2]; "normal" = N(0, std).
+* output gradient of the backward pass: dy ~ N(0, 1) [T][d], stored like x;
 * FP8 expert weights (weights == "fp8_e4m3"): the same float32 draws, quantised per output
   row: scale = max |row| / 448 (the largest E4M3 value), codes = torch's float8_e4m3fn
   cast (round to nearest) of row / scale. This is how a checkpoint would be converted; the
@@ -33,7 +34,7 @@ import numpy as np
 
 from .configs import LayerConfig
 
-TAG_X, TAG_WR, TAG_BIAS, TAG_WG, TAG_WU, TAG_WD, TAG_SWG, TAG_SWU, TAG_SWD, TAG_PERM = range(10)
+TAG_X, TAG_WR, TAG_BIAS, TAG_WG, TAG_WU, TAG_WD, TAG_SWG, TAG_SWU, TAG_SWD, TAG_PERM, TAG_DY = range(11)
 
 
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -192,6 +193,12 @@ def router_bias_values(cfg: LayerConfig) -> Optional[np.ndarray]:
     if cfg.router_bias == "normal":
         return _normal(cfg.seed, TAG_BIAS, 0, (E,), cfg.bias_scale)
     raise ValueError(f"unknown router bias recipe {cfg.router_bias!r}")
+
+
+def output_grad(cfg: LayerConfig) -> np.ndarray:
+    """dy [T][d] for the backward pass (storage format of x)."""
+    a = _normal(cfg.seed, TAG_DY, cfg.x_stream, (cfg.T, cfg.d_model), 1.0)
+    return to_bf16_bits(a) if cfg.dtype == "bf16" else a
 
 
 def make_inputs(cfg: LayerConfig) -> LayerInputs:

@@ -219,3 +219,52 @@ def test_fp8_workspace_is_the_dtype_layer_workspace():
         dt = cfg.replace(weights="dtype")
         for op in (binding.MOE_OP_GROUPED_MLP, binding.MOE_OP_LAYER):
             assert binding.moe_workspace_size(cfg, op) == binding.moe_workspace_size(dt, op)
+
+
+def test_layer_grads_struct_layout(tmp_path):
+    src = tmp_path / "g.c"
+    src.write_text('#include "moe.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   "int main(void){ printf(\"%zu %zu %zu\\n\", sizeof(moe_layer_grads),"
+                   " offsetof(moe_layer_grads, dw_down), offsetof(moe_layer_grads, aux_loss)); return 0; }\n")
+    exe = tmp_path / "g"
+    subprocess.run(["gcc", "-Wall", "-Werror", f"-I{os.path.dirname(HEADER)}", str(src), "-o", str(exe)], check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    G = binding.MoeLayerGrads
+    assert out == [ctypes.sizeof(G), G.dw_down.offset, G.aux_loss.offset]
+
+
+@lib_built
+def test_backward_rejects_bad_arguments_before_touching_the_device():
+    lib = binding.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    g = binding.MoeLayerGrads(*([0x2000] * 10))
+
+    def bwd(cfg, grads=g, dy=fake, aux=0.0, ws_bytes=1 << 40, shared=(None, None, None)):
+        return lib.moe_layer_backward(ctypes.byref(cfg), fake, fake, None, fake, fake, fake, *shared, dy, aux,
+                                      ctypes.byref(grads) if grads is not None else None, fake, ws_bytes, None)
+
+    assert bwd(_cfg(dtype=binding.MOE_F32)) == binding.MOE_ERR_UNSUPPORTED
+    assert bwd(_cfg(), aux=float("nan")) == binding.MOE_ERR_INVALID_ARG
+    assert bwd(_cfg(), dy=None) == binding.MOE_ERR_INVALID_ARG
+    assert bwd(_cfg(), grads=None) == binding.MOE_ERR_INVALID_ARG
+    assert bwd(_cfg(), grads=binding.MoeLayerGrads(0x2000, None, *([0x2000] * 8))) == binding.MOE_ERR_INVALID_ARG
+    sh = _cfg(n_shared=1, d_ff_shared=128)
+    assert bwd(sh) == binding.MOE_ERR_INVALID_ARG  # no shared weights
+    assert bwd(sh, shared=(fake, fake, fake),
+               grads=binding.MoeLayerGrads(*([0x2000] * 6), None, None, None, None)) == binding.MOE_ERR_INVALID_ARG
+    assert bwd(_cfg(), ws_bytes=16) == binding.MOE_ERR_WORKSPACE
+    assert lib.moe_layer_backward(ctypes.byref(_cfg(T=0)), *([None] * 10), 0.0, None, None, 0, None) == binding.MOE_OK
+    # the optional outputs may be NULL
+    opt = binding.MoeLayerGrads(0x2000, 0x2000, None, 0x2000, 0x2000, 0x2000, None, None, None, None)
+    assert bwd(_cfg(), grads=opt, ws_bytes=16) == binding.MOE_ERR_WORKSPACE
+
+
+@lib_built
+def test_backward_workspace_sizes():
+    for cfg in (configs.MIXTRAL_PREFILL, configs.QWEN3_FINE, configs.DEEPSEEK_V3):
+        b = binding.moe_workspace_size(cfg, binding.MOE_OP_LAYER_BACKWARD)
+        assert b % 256 == 0
+        # holds at least the transposed expert weights
+        assert b >= cfg.n_experts * 3 * cfg.d_model * cfg.d_ff * 2
+    with pytest.raises(binding.MoeError):
+        binding.moe_workspace_size(configs.TINY_FP32, binding.MOE_OP_LAYER_BACKWARD)
