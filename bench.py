@@ -81,14 +81,16 @@ def traffic_from_profile(kernel_file: str, workload: str):
     return None
 
 
-def time_steps(step, K: int, warmup: int, stream):
-    """Warm up, then time exactly K calls of step() on `stream`, bracketing the gated launch
-    of each with HIP events (moe_time_next_launch). Returns (wall seconds, per-step ms,
-    per-step gated-launch ms)."""
+def time_steps(step, K: int, warmup: int, stream, kernel=None):
+    """Warm up, then time exactly K calls of step() on `stream`, bracketing one launch of
+    `kernel` (default: the gated launch) in each with HIP events (moe_time_next_launch).
+    Returns (wall seconds, per-step ms, per-step ms of that launch)."""
     import numpy as np
     import torch
 
     from sparse_mixture_experts_29_amd import binding
+    if kernel is None:
+        kernel = binding.MOE_KERNEL_GATE_UP
     ev = HipEvents()
     for _ in range(warmup):
         step()
@@ -100,7 +102,7 @@ def time_steps(step, K: int, warmup: int, stream):
     t0 = time.perf_counter()
     step_ev[0].record(stream)
     for i in range(K):
-        binding.moe_time_next_launch(binding.MOE_KERNEL_GATE_UP, begins[i], ends[i])
+        binding.moe_time_next_launch(kernel, begins[i], ends[i])
         step()
         step_ev[i + 1].record(stream)
     torch.cuda.synchronize()
@@ -187,6 +189,114 @@ def shard_bench(args, w):
     print(json.dumps(out), flush=True)
 
 
+def backward_bench(args, cfg):
+    """Training step of one layer: moe_layer_forward then moe_layer_backward (which recomputes
+    the routing and the gate/up products) for the seeded output gradient, inputs resident in
+    HBM. value = tokens per second of the step; roofline = the longest backward GEMM launch."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_29_amd import binding
+    from sparse_mixture_experts_29_amd.device import DeviceLayer, LayerGrads, host_to_device
+    from sparse_mixture_experts_29_amd.inputs import make_inputs, output_grad
+
+    binding.load_library()
+    li = make_inputs(cfg)
+    dev = DeviceLayer(li, device="cuda:0", threads=16)
+    dy = host_to_device(output_grad(cfg), cfg, dev.device)
+    grads = LayerGrads(dev)
+    aux = args.aux_coef
+    stream = torch.cuda.current_stream()
+    b = dev.stage_buffers()
+    dev.route(b, logits=False)
+    dev.permute(b)
+    torch.cuda.synchronize()
+    n_kept = int(b["offsets"][-1].item())
+    del b
+
+    def step():
+        dev.forward()
+        dev.backward(dy, aux, grads)
+
+    # per-kernel launch times (outside the timed steps): each backward GEMM in its own pass
+    kernels = [("recompute x Wg | x Wu", binding.MOE_KERNEL_BWD_RECOMPUTE, 4),
+               ("down dgrad u = dy Wd", binding.MOE_KERNEL_BWD_DOWN_DGRAD, 2),
+               ("gate/up dgrad (da|db)(Wg|Wu)", binding.MOE_KERNEL_BWD_GATE_UP_DGRAD, 4),
+               ("down wgrad", binding.MOE_KERNEL_BWD_DOWN_WGRAD, 2),
+               ("gate wgrad", binding.MOE_KERNEL_BWD_GATE_WGRAD, 2),
+               ("up wgrad", binding.MOE_KERNEL_BWD_UP_WGRAD, 2)]
+    per = {}
+    for name, kid, mult in kernels:
+        _, _, ms = time_steps(step, 5, 1 if per else args.warmup, stream, kernel=kid)
+        flops = mult * (cfg.d_model * cfg.d_ff * n_kept + cfg.d_model * cfg.d_ff_shared * cfg.T * cfg.n_shared)
+        per[name] = dict(kernel_id=kid, avg_launch_ms=round(float(ms.mean()), 4), flops_per_launch=float(flops),
+                         tflops=round(flops / (ms.mean() * 1e-3) / 1e12, 1))
+    dom_name = max(per, key=lambda n: per[n]["avg_launch_ms"])
+    dom = per[dom_name]
+    elapsed, step_ms, dom_ms = time_steps(step, args.steps, 0, stream, kernel=dom["kernel_id"])
+    K = args.steps
+    achieved = dom["flops_per_launch"] / (dom_ms.mean() * 1e-3) / 1e12
+    train_flops = 22.0 * cfg.d_model * cfg.d_ff * n_kept + 22.0 * cfg.d_model * cfg.d_ff_shared * cfg.T * cfg.n_shared
+    out = {
+        "metric": "training-step tokens/sec per MoE layer (forward + backward with recompute)",
+        "value": round(cfg.T * K / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations and output gradient, N(0,1/sqrt(fan_in)) random-init weights)",
+        "config": {"workload": cfg.name + "_train", "T": cfg.T, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
+                   "n_experts": cfg.n_experts, "top_k": cfg.top_k, "gating": cfg.gating,
+                   "capacity_factor": cfg.capacity_factor, "n_shared": cfg.n_shared,
+                   "d_ff_shared": cfg.d_ff_shared, "aux_coef": aux, "parallelism": "single GPU"},
+        "roofline": {"kernel": f"grouped_gemm_bf16 ({dom_name})", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(float(dom_ms.mean()), 4),
+                     "flops_per_launch": dom["flops_per_launch"]},
+        "layer": {
+            "step_ms_p50": round(float(np.percentile(step_ms, 50)), 4),
+            "step_ms_p95": round(float(np.percentile(step_ms, 95)), 4),
+            "step_ms_p99": round(float(np.percentile(step_ms, 99)), 4),
+            "train_step_tflops": round(train_flops / (np.median(step_ms) * 1e-3) / 1e12, 2),
+            "n_kept": n_kept,
+            "backward_gemms": per,
+        },
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_backward(li, min(args.cpu_tokens, cfg.T), aux)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_backward(li, n_tokens: int, aux: float):
+    """The oracle's forward and backward (as they stand) on the first n_tokens of the workload."""
+    import threadpoolctl
+
+    import oracle
+    from sparse_mixture_experts_29_amd.inputs import output_grad
+    c = li.cfg
+    x = li.values(li.x[:n_tokens])
+    dy = li.values(output_grad(c)[:n_tokens])
+    wr = li.values(li.w_router)
+    experts = [li.expert_values(e) for e in range(c.n_experts)]  # input generation: untimed
+    shared = [li.shared_values(s) for s in range(c.n_shared)]
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    oracle.forward(x, wr, li.router_bias, top_k=c.top_k, gating=c.gating, capacity_factor=c.capacity_factor,
+                   experts=experts, shared=shared, n_shared=c.n_shared)
+    oracle.backward(x, wr, li.router_bias, dy, top_k=c.top_k, gating=c.gating, capacity_factor=c.capacity_factor,
+                    experts=experts, shared=shared, n_shared=c.n_shared, aux_coef=aux)
+    dt = time.perf_counter() - t0
+    return dict(value=n_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"forward + backward of the first {n_tokens} of {c.T} tokens of {c.name} "
+                       f"(capacity and balancing loss over that sample); {dt:.1f} s", seconds=round(dt, 2))
+
+
 def cpu_baseline(li, n_tokens: int):
     """The oracle (as it stands) on the first n_tokens of the workload, on host cores."""
     import numpy as np
@@ -228,6 +338,9 @@ def main():
     ap.add_argument("--workload", default=None, help="name of a configs.ALL or configs.SHARDS entry")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the training step (forward + moe_layer_backward) of the workload")
+    ap.add_argument("--aux-coef", type=float, default=0.01, help="balancing-loss coefficient (--backward)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many MiB once (a plain copy "
                          "kernel of known size, to scale the HBM byte counters of a profiler run)")
@@ -247,6 +360,10 @@ def main():
     if args.workload in configs.SHARDS:
         return shard_bench(args, configs.SHARDS[args.workload])
     cfg = configs.ALL[args.workload] if args.workload else configs.MIXTRAL_PREFILL
+    if args.backward:
+        if args.cpu_tokens == 4096:
+            args.cpu_tokens = 512
+        return backward_bench(args, cfg)
     binding.load_library()
     li = make_inputs(cfg)
     t_gen = time.perf_counter()

@@ -134,3 +134,85 @@ def test_backward_leaves_the_forward_inputs_untouched():
     for a, b in zip(before, (dev.x, dev.w_router, dev.w_gate, dev.w_up, dev.w_down)):
         assert torch.equal(a, b)
     assert torch.equal(y0, y1)
+
+
+def check_backward_sampled(li, dev, g, idx_g, aux, n_tokens=6, n_experts=2, n_cols=48, seed=0):
+    """Full-size layer: weight gradients of sampled experts on sampled f-indices (an expert's
+    FFN separates over f, so the oracle's swiglu_backward on rows M of Wg, Wu and columns M of
+    Wd returns exactly the rows M of dWg, dWu and the columns M of dWd), dx on sampled tokens
+    (their pairs' dv, the router term and the shared experts), and the balancing loss."""
+    c = li.cfg
+    rng = np.random.default_rng([seed, c.T])
+    x = li.values(li.x)
+    dy = li.values(output_grad(c))
+    wr = li.values(li.w_router)
+    make_expert, shared = P.oracle_weights(li)
+    cache = {}
+
+    def experts(e):  # each expert's weights are drawn once
+        if e not in cache:
+            cache[e] = make_expert(e)
+        return cache[e]
+
+    logits = oracle.router_logits(x, wr, li.router_bias)
+    gate = oracle.gate_values(logits, idx_g, c.gating)
+    cap = oracle.expert_capacity(c.capacity_factor, c.T, c.top_k, c.n_experts)
+    perm = oracle.permute(idx_g, c.n_experts, cap)
+    keep = (perm["drop"] == 0).reshape(c.T, c.top_k)
+    h = P.host
+    counts = np.diff(perm["offsets"])
+    nonempty = np.flatnonzero(counts > 0)
+    picks = [int(nonempty[np.argmax(counts[nonempty])])]
+    picks += [int(e) for e in rng.choice(nonempty, size=min(len(nonempty), n_experts) - 1, replace=False)
+              if int(e) not in picks]
+    dwg, dwu, dwd = g.dw_gate, g.dw_up, g.dw_down
+    for e in picks:
+        wg, wu, wd = experts(e)
+        rows_t, rows_j = np.nonzero((idx_g == e) & keep)
+        M = np.unique(np.concatenate([[0, c.d_ff - 1], rng.choice(c.d_ff, size=n_cols, replace=False)]))
+        dyp = gate[rows_t, rows_j][:, None] * dy[rows_t]
+        _, _, dwg_m, dwu_m, dwd_m = oracle.swiglu_backward(x[rows_t], wg[M], wu[M], wd[:, M], dyp)
+        Mt = torch.as_tensor(M, device=dwg.device)
+        close(h(dwg[e].index_select(0, Mt)), dwg_m, f"dw_gate[{e}] rows")
+        close(h(dwu[e].index_select(0, Mt)), dwu_m, f"dw_up[{e}] rows")
+        close(h(dwd[e].index_select(1, Mt)), dwd_m, f"dw_down[{e}] columns")
+    toks = np.unique(np.concatenate([[0, c.T - 1], rng.integers(0, c.T, size=n_tokens)]))
+    loss, dl_aux = oracle.aux_loss(logits, perm["counts"], c.top_k, c.gating, aux) if aux else (0.0, None)
+    want = np.zeros((len(toks), c.d_model))
+    for n, t in enumerate(toks):
+        dg = np.zeros(c.top_k)
+        for j in range(c.top_k):
+            if not keep[t, j]:
+                continue
+            y_p, dv, _, _, _ = oracle.swiglu_backward(x[t:t + 1], *experts(int(idx_g[t, j])), gate[t, j] * dy[t:t + 1])
+            want[n] += dv[0]
+            dg[j] = float((dy[t] * y_p[0]).sum())
+        dl = oracle.gate_backward(logits[t:t + 1], idx_g[t:t + 1], gate[t:t + 1], dg[None, :], c.gating)[0]
+        if dl_aux is not None:
+            dl = dl + dl_aux[t]
+        want[n] += dl @ wr
+        for s_ in range(c.n_shared):
+            want[n] += oracle.swiglu_backward(x[t:t + 1], *shared(s_), dy[t:t + 1])[1][0]
+    close(h(g.dx.index_select(0, torch.as_tensor(toks, device=g.dx.device))), want, "dx (sampled tokens)")
+    if aux:
+        assert abs(float(g.aux_loss.item()) - loss) <= 1e-4 * abs(loss)
+    P.say(f"  sampled experts {picks}, tokens {len(toks)}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [configs.MIXTRAL_PREFILL, configs.QWEN3_FINE_CF], ids=lambda c: c.name)
+def test_backward_full_size_sampled(cfg):
+    """The launch configuration the training-step benchmark times (aux_coef 0.01)."""
+    P.say(f"case {cfg.name}: generating {cfg.total_weight_bytes() / 1e9:.2f} GB of weights")
+    li = make_inputs(cfg)
+    dev = DeviceLayer(li, threads=16)
+    dy = host_to_device(output_grad(cfg), cfg, dev.device)
+    b = dev.stage_buffers()
+    dev.route(b)
+    torch.cuda.synchronize()
+    r = P.check_route(li, dev, b)
+    del b
+    g = dev.backward(dy, 0.01)
+    torch.cuda.synchronize()
+    P.say("  backward done")
+    check_backward_sampled(li, dev, g, r["idx"], 0.01)
