@@ -115,6 +115,7 @@ struct BwdWs {
   void* dx_s;                       // [n_s + 1][T][d]: shared experts' dx, then the router's
   float* dl;                        // [T][E]
   float* aux_part;                  // [T]
+  float* rpart;                     // split-K partials of the router gradients
   int32_t* poff;                    // [E+1]
   void *dypT, *xgT, *hT, *dabT;     // [C][np]: routed segments
   void *dyT, *xT, *hsT, *dabsT;     // [C][tp] ([n_s][C][tp]): shared experts' token rows
@@ -165,6 +166,7 @@ BwdWs bwd_layout(const Shape& s, void* base) {
   w.dx_s = take((ns + 1) * T * d * 2);
   w.dl = reinterpret_cast<float*>(take(T * E * 4));
   w.aux_part = reinterpret_cast<float*>(take(T * 4));
+  w.rpart = reinterpret_cast<float*>(take(std::max(fma_gemm_ws_bytes(s.E, s.d, s.T), fma_gemm_ws_bytes(s.T, s.d, s.E))));
   w.poff = reinterpret_cast<int32_t*>(take((E + 1) * 4));
   w.dypT = take(d * np * 2);
   w.xgT = take(d * np * 2);
@@ -574,8 +576,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
   if (e == hipSuccess)
     e = launch_router_bwd(s, w.logits, w.idx, w.gate, w.d_gate, w.counts, aux_coef, w.dl, w.aux_part, g->aux_loss,
                           g->d_router_bias, st);
-  if (e == hipSuccess) e = launch_fma_gemm(w.dl, 1, E, x, d, E, d, s.T, g->dw_router, d, st);
-  if (e == hipSuccess) e = launch_fma_gemm(w.dl, E, 1, w_router, d, s.T, d, E, dx_router, d, st);
+  if (e == hipSuccess) e = launch_fma_gemm(w.dl, 1, E, x, d, E, d, s.T, g->dw_router, d, w.rpart, st);
+  if (e == hipSuccess) e = launch_fma_gemm(w.dl, E, 1, w_router, d, s.T, d, E, dx_router, d, w.rpart, st);
   // (6) dx = every kept pair's dx + shared experts' + router's (a combine with unit gates)
   if (e == hipSuccess) {
     Shape s2 = s;

@@ -345,36 +345,48 @@ __global__ __launch_bounds__(256) void sum_kernel(const float* __restrict__ v, i
   if (threadIdx.x == 0) out[0] = red[0];
 }
 
-// out[e] = sum over t of m[t][e], t ascending.
+// out[e] = sum over t of m[t][e]: one block per e, thread i sums the rows t = i mod 256 in
+// ascending order, then a fixed tree over the 256 partial sums.
 __global__ __launch_bounds__(256) void col_sum_kernel(const float* __restrict__ m, int64_t T, int E,
                                                       float* __restrict__ out) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
+  __shared__ float red[256];
+  const int e = blockIdx.x;
   float s = 0.f;
-  for (int64_t t = 0; t < T; ++t) s += m[t * E + e];
-  out[e] = s;
+  for (int64_t t = threadIdx.x; t < T; t += 256) s += m[t * E + e];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[e] = red[0];
 }
 
 // C[m][n] = sum_k A(m, k) B(k, n), A(m, k) = A[m*sam + k*sak] (fp32), B(k, n) = B[k*ldb + n]
-// (bf16), rounded once to bf16. 64 x 64 tiles, 16 x 16 threads of 4 x 4 outputs, K in
-// chunks of 16 through LDS. For the router's weight and input gradients (E columns).
+// (bf16). 64 x 64 tiles, 16 x 16 threads of 4 x 4 outputs, K in chunks of 16 through LDS.
+// Block z covers k in [z*kc, (z+1)*kc): with one split the result is rounded once to bf16
+// into C; with several, each writes its fp32 partial P[z][m][n] and reduce_splits_kernel
+// sums them in split order. For the router's weight and input gradients.
 __global__ __launch_bounds__(256) void fma_gemm_kernel(const float* __restrict__ A, int64_t sam, int64_t sak,
                                                        const bf16_t* __restrict__ B, int64_t ldb, int64_t M, int N,
-                                                       int64_t K, bf16_t* __restrict__ C, int64_t ldc) {
+                                                       int64_t K, int64_t kc, bf16_t* __restrict__ C, int64_t ldc,
+                                                       float* __restrict__ P) {
   __shared__ float As[16][65], Bs[16][65];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 64;
   const int n0 = blockIdx.x * 64;
+  const int64_t kb = static_cast<int64_t>(blockIdx.z) * kc;
+  const int64_t ke = kb + kc < K ? kb + kc : K;
   float c[4][4] = {};
-  for (int64_t k0 = 0; k0 < K; k0 += 16) {
+  for (int64_t k0 = kb; k0 < ke; k0 += 16) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = threadIdx.x + q * 256;  // 1024 = 16 x 64
       const int kk = i >> 6, mm = i & 63;
       const int64_t gm = m0 + mm, gk = k0 + kk;
-      As[kk][mm] = gm < M && gk < K ? A[gm * sam + gk * sak] : 0.f;
+      As[kk][mm] = gm < M && gk < ke ? A[gm * sam + gk * sak] : 0.f;
       const int gn = n0 + mm;
-      Bs[kk][mm] = gn < N && gk < K ? bf16_to_f32(B[gk * ldb + gn]) : 0.f;
+      Bs[kk][mm] = gn < N && gk < ke ? bf16_to_f32(B[gk * ldb + gn]) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -399,9 +411,23 @@ __global__ __launch_bounds__(256) void fma_gemm_kernel(const float* __restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int gn = n0 + tx * 4 + j;
-      if (gn < N) C[gm * ldc + gn] = f32_to_bf16(c[i][j]);
+      if (gn >= N) continue;
+      if (P != nullptr)
+        P[(static_cast<int64_t>(blockIdx.z) * M + gm) * N + gn] = c[i][j];
+      else
+        C[gm * ldc + gn] = f32_to_bf16(c[i][j]);
     }
   }
+}
+
+// C[m][n] = bf16(sum over z < splits of P[z][m][n]), z ascending.
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ P, int splits, int64_t M,
+                                                            int N, bf16_t* __restrict__ C, int64_t ldc) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= M * N) return;
+  float s = 0.f;
+  for (int z = 0; z < splits; ++z) s += P[z * M * N + i];
+  C[(i / N) * ldc + i % N] = f32_to_bf16(s);
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
@@ -456,15 +482,33 @@ hipError_t launch_router_bwd(const Shape& s, const float* logits, const int32_t*
   hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks(s.T, 4)), dim3(256), 0, st, logits, idx, gate, d_gate, counts,
                      s.T, s.E, s.k, s.gating, aux_coef, dl, aux_part);
   if (aux_loss != nullptr) hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(256), 0, st, aux_part, s.T, aux_loss);
-  if (d_bias != nullptr) hipLaunchKernelGGL(col_sum_kernel, dim3(blocks(s.E, 256)), dim3(256), 0, st, dl, s.T, s.E, d_bias);
+  if (d_bias != nullptr) hipLaunchKernelGGL(col_sum_kernel, dim3(s.E), dim3(256), 0, st, dl, s.T, s.E, d_bias);
   return hipGetLastError();
 }
 
+int fma_gemm_splits(int64_t M, int N, int64_t K) {
+  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int64_t sp = (1024 + tiles - 1) / tiles;      // about 1024 blocks in all
+  sp = std::min<int64_t>(sp, (K + 255) / 256);  // each split keeps >= 256 of K
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(sp, 32)));
+}
+
+size_t fma_gemm_ws_bytes(int64_t M, int N, int64_t K) {
+  const int sp = fma_gemm_splits(M, N, K);
+  return sp > 1 ? static_cast<size_t>(sp) * M * N * sizeof(float) : 0;
+}
+
 hipError_t launch_fma_gemm(const float* A, int64_t sam, int64_t sak, const void* B, int64_t ldb, int64_t M, int N,
-                           int64_t K, void* C, int64_t ldc, hipStream_t st) {
+                           int64_t K, void* C, int64_t ldc, float* partials, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fma_gemm_kernel, dim3(blocks(N, 64), blocks(M, 64)), dim3(256), 0, st, A, sam, sak,
-                     static_cast<const bf16_t*>(B), ldb, M, N, K, static_cast<bf16_t*>(C), ldc);
+  const int sp = fma_gemm_splits(M, N, K);
+  const int64_t kc = ((K + sp - 1) / sp + 15) / 16 * 16;
+  float* P = sp > 1 ? partials : nullptr;
+  hipLaunchKernelGGL(fma_gemm_kernel, dim3(blocks(N, 64), blocks(M, 64), sp), dim3(256), 0, st, A, sam, sak,
+                     static_cast<const bf16_t*>(B), ldb, M, N, K, kc, static_cast<bf16_t*>(C), ldc, P);
+  if (sp > 1)
+    hipLaunchKernelGGL(reduce_splits_kernel, dim3(blocks(M * N, 256)), dim3(256), 0, st, P, sp, M, N,
+                       static_cast<bf16_t*>(C), ldc);
   return hipGetLastError();
 }
 

@@ -156,8 +156,10 @@ hipError_t launch_swiglu_bwd(const Shape& s, const void* ab, const void* u, cons
 hipError_t launch_router_bwd(const Shape& s, const float* logits, const int32_t* idx, const float* gate,
                              const float* d_gate, const int32_t* counts, float aux_coef, float* dl, float* aux_part,
                              float* aux_loss, float* d_bias, hipStream_t st);
+// split-K over ~1024 blocks when M x N is small; partials: fma_gemm_ws_bytes of fp32
+size_t fma_gemm_ws_bytes(int64_t M, int N, int64_t K);
 hipError_t launch_fma_gemm(const float* A, int64_t sam, int64_t sak, const void* B, int64_t ldb, int64_t M, int N,
-                           int64_t K, void* C, int64_t ldc, hipStream_t st);
+                           int64_t K, void* C, int64_t ldc, float* partials, hipStream_t st);
 hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st);
 
 struct TimingRequest {
