@@ -51,20 +51,74 @@ struct SmallArgs {
   int64_t max_kept;
 };
 
-// K loop and epilogue of one unit with NG (compile-time) token groups of 16. Operands of
-// K block i+D-1 (weights and token rows) are loaded while block i is multiplied: a ring of
-// D register sets, so no load waits on the one before it.
+// Ring depths (DW, DX) of the K loop per launch kind: gated (G) or down (D), bf16 (B) or
+// FP8 (F) weights, NG token groups. The weights of block i+DW-1 and the token rows of block
+// i+DX-1 are loaded while block i is multiplied. DX divides DW. Measured on the Mixtral-shaped
+// decode layer (T = 1..64, bf16 and FP8): equal depths, 3 (5 for one FP8 token group), are
+// the fastest; a shorter token-row lead with a deeper weight ring (4/2, 6/2, 6/3, 8/2, 8/4)
+// was equal or slower everywhere.
+#ifndef MOE_SM_GB1
+#define MOE_SM_GB1 3, 3
+#endif
+#ifndef MOE_SM_GB2
+#define MOE_SM_GB2 3, 3
+#endif
+#ifndef MOE_SM_DB1
+#define MOE_SM_DB1 3, 3
+#endif
+#ifndef MOE_SM_DB2
+#define MOE_SM_DB2 3, 3
+#endif
+#ifndef MOE_SM_GF1
+#define MOE_SM_GF1 5, 5
+#endif
+#ifndef MOE_SM_GF2
+#define MOE_SM_GF2 3, 3
+#endif
+#ifndef MOE_SM_DF1
+#define MOE_SM_DF1 5, 5
+#endif
+#ifndef MOE_SM_DF2
+#define MOE_SM_DF2 3, 3
+#endif
+template <bool GATED, int NG, bool FP8>
+struct RingDepth {
+  static constexpr int v[2] = {MOE_SM_GB1};
+};
+#define MOE_SM_RING(G, N, F, DEPTHS)          \
+  template <>                                 \
+  struct RingDepth<G, N, F> {                 \
+    static constexpr int v[2] = {DEPTHS};     \
+  };
+MOE_SM_RING(true, 2, false, MOE_SM_GB2)
+MOE_SM_RING(false, 1, false, MOE_SM_DB1)
+MOE_SM_RING(false, 2, false, MOE_SM_DB2)
+MOE_SM_RING(true, 1, true, MOE_SM_GF1)
+MOE_SM_RING(true, 2, true, MOE_SM_GF2)
+MOE_SM_RING(false, 1, true, MOE_SM_DF1)
+MOE_SM_RING(false, 2, true, MOE_SM_DF2)
+#undef MOE_SM_RING
+
+// K loop and epilogue of one unit with NG (compile-time) token groups of 16: weights DW-1
+// blocks ahead, token rows DX-1 blocks ahead of the multiply, so no load waits on the one
+// issued before it.
 // FP8 (E4M3) weights: a lane's 32 k values of a block are 32 bytes (two 16-byte loads) and
 // are widened to bf16 exactly (every E4M3 value is a bf16 value) right before the multiply;
 // the per-row scale multiplies the accumulator in the epilogue.
-template <bool GATED, int NG, int D, bool FP8>
+template <bool GATED, int NG, bool FP8>
 __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const void* w0, const void* w1,
                                              const bf16_t* const (&xp)[2], int t0, int kbeg, int kend,
                                              int quad, int l16, int M, int r0, int gi, bool shared,
                                              int N, int n0, int split) {
   constexpr int NW = FP8 ? 2 : 4;  // 16-byte weight loads per lane per block and matrix
-  struct Ops {
-    u32x4 wa[NW], wb[NW], xv[NG][4];
+  constexpr int DW = RingDepth<GATED, NG, FP8>::v[0];
+  constexpr int DX = RingDepth<GATED, NG, FP8>::v[1];
+  static_assert(DX >= 1 && DW >= DX && DW % DX == 0, "the token-row ring divides the weight ring");
+  struct WOps {
+    u32x4 wa[NW], wb[NW];
+  };
+  struct XOps {
+    u32x4 xv[NG][4];
   };
   // A operand c of a block (k = ko + 8c .. +8), from the raw weight registers; m zeroes the
   // dead lanes of the tail block (FP8 code 0 is +0)
@@ -99,77 +153,114 @@ __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const void* w0,
   // instead, which is in range, and the multiply zeroes what they read. Loads are issued
   // unconditionally and left untouched until their block is multiplied, so the compiler's
   // count of loads in flight stays exact and no wait drains the ring.
-  auto load = [&](Ops& o, int kb, bool full) {
-    const int ko = kb + (full || quad < 2 ? quad * 32 : 0);
+  auto offs = [&](int kb, bool full) { return kb + (full || quad < 2 ? quad * 32 : 0); };
+  auto load_w = [&](WOps& o, int kb, bool full) {
+    const int ko = offs(kb, full);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NW; ++c) {
       if constexpr (FP8) {
-        if (c < NW) {
-          o.wa[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w0) + ko + c * 16);
-          if (GATED) o.wb[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w1) + ko + c * 16);
-        }
+        o.wa[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w0) + ko + c * 16);
+        if (GATED) o.wb[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w1) + ko + c * 16);
       } else {
         o.wa[c] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(w0) + ko + c * 8);
         if (GATED) o.wb[c] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(w1) + ko + c * 8);
       }
-#pragma unroll
-      for (int t = 0; t < NG; ++t) o.xv[t][c] = *reinterpret_cast<const u32x4*>(xp[t] + ko + c * 8);
     }
   };
+  auto load_x = [&](XOps& o, int kb, bool full) {
+    const int ko = offs(kb, full);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < NG; ++t) o.xv[t][c] = *reinterpret_cast<const u32x4*>(xp[t] + ko + c * 8);
+  };
   // m: all ones, or zero for the dead lanes of the tail block
-  auto mma = [&](const Ops& o, unsigned m) {
+  auto mma = [&](const WOps& w, const XOps& o, unsigned m) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
         const bf16x8 x = __builtin_bit_cast(bf16x8, o.xv[t][c] & m);
-        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop(o.wa, c, m), x, acc0[t], 0, 0, 0);
-        if (GATED) acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop(o.wb, c, m), x, acc1[t], 0, 0, 0);
+        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop(w.wa, c, m), x, acc0[t], 0, 0, 0);
+        if (GATED) acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop(w.wb, c, m), x, acc1[t], 0, 0, 0);
       }
   };
-  auto mma_full = [&](const Ops& o) {
+  auto mma_full = [&](const WOps& w, const XOps& o) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
         const bf16x8 x = __builtin_bit_cast(bf16x8, o.xv[t][c]);
-        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfull(o.wa, c), x, acc0[t], 0, 0, 0);
-        if (GATED) acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfull(o.wb, c), x, acc1[t], 0, 0, 0);
+        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfull(w.wa, c), x, acc0[t], 0, 0, 0);
+        if (GATED) acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfull(w.wb, c), x, acc1[t], 0, 0, 0);
       }
   };
   const int nfull = (kend - kbeg) / 128;        // full 128-wide blocks
   const bool tail = (kend - kbeg) % 128 != 0;   // then a 64-wide block
   const int nb = nfull + (tail ? 1 : 0);
-  auto load_block = [&](Ops& o, int b) { load(o, kbeg + b * 128, b < nfull); };
-  auto mma_block = [&](const Ops& o, int b) { mma(o, b < nfull || quad < 2 ? 0xFFFFFFFFu : 0u); };
-  // ring of D register sets: on entry to an iteration blocks i .. i+D-2 sit in o[0 .. D-2].
-  // The steady loop runs while every block it loads exists (no guards inside) and never
-  // multiplies the tail block; the peeled round after it finishes the last < 2D-1 blocks.
-  Ops o[D];
-  // unconditional (a unit of fewer than D-1 blocks reloads its last one): no branch ahead of
-  // the loop, so the wait counts inside it stay exact
+  // the weights of block bw and the token rows of block bx, interleaved chunk by chunk (so
+  // the registers freed by one chunk's loads are reused by the next: no spills)
+  auto load_wx = [&](WOps& w, int bw, XOps& o, int bx) {
+    const int kw = offs(kbeg + bw * 128, bw < nfull), kx = offs(kbeg + bx * 128, bx < nfull);
 #pragma unroll
-  for (int j = 0; j < D - 1; ++j) load_block(o[j], min(j, nb - 1));
+    for (int c = 0; c < 4; ++c) {
+      if (c < NW) {
+        if constexpr (FP8) {
+          w.wa[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w0) + kw + c * 16);
+          if (GATED) w.wb[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w1) + kw + c * 16);
+        } else {
+          w.wa[c] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(w0) + kw + c * 8);
+          if (GATED) w.wb[c] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(w1) + kw + c * 8);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NG; ++t) o.xv[t][c] = *reinterpret_cast<const u32x4*>(xp[t] + kx + c * 8);
+    }
+  };
+  auto load_wb = [&](WOps& o, int b) { load_w(o, kbeg + b * 128, b < nfull); };
+  auto load_xb = [&](XOps& o, int b) { load_x(o, kbeg + b * 128, b < nfull); };
+  auto mma_block = [&](const WOps& w, const XOps& o, int b) {
+    mma(w, o, b < nfull || quad < 2 ? 0xFFFFFFFFu : 0u);
+  };
+  // rings: on entry to an iteration, the weights of blocks i .. i+DW-2 sit in W and the token
+  // rows of blocks i .. i+DX-2 in X (block b in W[b % DW], X[b % DX]). The steady loop runs
+  // while every block it loads exists (no guards inside) and never multiplies the tail block;
+  // the peeled rounds after it finish the last < 2 DW - 1 blocks.
+  WOps W[DW];
+  XOps X[DX];
+  // unconditional (a unit of fewer blocks reloads its last one): no branch ahead of the loop,
+  // so the wait counts inside it stay exact
+#pragma unroll
+  for (int j = 0; j < DW - 1; ++j) {
+    if (j < DX - 1)
+      load_wx(W[j], min(j, nb - 1), X[j], min(j, nb - 1));
+    else
+      load_wb(W[j], min(j, nb - 1));
+  }
   int i = 0;
-  for (; i + 2 * D - 1 <= nb; i += D) {
+  for (; i + 2 * DW - 1 <= nb; i += DW) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      // issue block i+j+D-1 before multiplying block i+j; the scheduling barriers stop the
-      // compiler from hoisting the next block's multiplies above these loads
-      load_block(o[(j + D - 1) % D], i + j + D - 1);
+    for (int j = 0; j < DW; ++j) {
+      // issue block i+j+DW-1's weights and block i+j+DX-1's token rows before multiplying
+      // block i+j; the scheduling barriers stop the compiler from hoisting the next block's
+      // multiplies above these loads
+      load_wx(W[(j + DW - 1) % DW], i + j + DW - 1, X[(j + DX - 1) % DX], i + j + DX - 1);
       __builtin_amdgcn_sched_barrier(0);
-      mma_full(o[j]);
+      mma_full(W[j], X[j % DX]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    if (i + j + D - 1 < nb) load_block(o[(j + D - 1) % D], i + j + D - 1);
-    if (i + j < nb) mma_block(o[j], i + j);
+  for (int j = 0; j < DW; ++j) {
+    if (i + j + DW - 1 < nb) load_wb(W[(j + DW - 1) % DW], i + j + DW - 1);
+    if (i + j + DX - 1 < nb) load_xb(X[(j + DX - 1) % DX], i + j + DX - 1);
+    if (i + j < nb) mma_block(W[j], X[j % DX], i + j);
   }
 #pragma unroll
-  for (int j = 0; j < D - 1; ++j)
-    if (i + D + j < nb) mma_block(o[j], i + D + j);
+  for (int j = 0; j < DW - 1; ++j) {
+    if (i + DW + j + DX - 1 < nb) load_xb(X[(j + DX - 1) % DX], i + DW + j + DX - 1);
+    if (i + DW + j < nb) mma_block(W[j], X[j % DX], i + DW + j);
+  }
 
   // epilogue. 16x16 C layout: lane holds weight rows n0 + 4*quad + r (r = 0..3) for token
   // column l16 of each group.
@@ -280,12 +371,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       src = GATED ? a.sorted_slot[r] / a.k : r;
     xp[t] = in + src * K;
   }
-  // FP8 blocks carry half the weight bytes: a deeper ring keeps as many bytes in flight
   if (NGW == 1 || ng <= 1)
-    small_m_unit<GATED, 1, FP8 ? 5 : 3, FP8>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0,
-                                            split);
+    small_m_unit<GATED, 1, FP8>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split);
   else
-    small_m_unit<GATED, 2, 3, FP8>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split);
+    small_m_unit<GATED, 2, FP8>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split);
 }
 
 // h = silu(sum of gate partials) * (sum of up partials), the sums over K splits in split
