@@ -371,6 +371,17 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
                                   w.gate, y, st);
     return hip_status(e);
   }
+  const int sp = large_down_splits(s);
+  if (sp > 1) {
+    // split-K down launch: combine from its fp32 partials (the same sums and roundings as the
+    // reduction into y_perm of the staged calls)
+    if (e == hipSuccess)
+      e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, nullptr,
+                             nullptr, w.grouped_ws, st);
+    if (e == hipSuccess)
+      e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), sp, w.pos, w.gate, y, st);
+    return hip_status(e);
+  }
   if (e == hipSuccess)
     e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, w_gate, w_up, w_down, ws_gate, ws_up,
                            ws_down, w.y_perm, w.y_shared, w.grouped_ws, st);
@@ -401,6 +412,15 @@ moe_status moe_expert_shard_forward(const moe_config* cfg, const void* x_recv, c
     if (e == hipSuccess)
       e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false), w.pos,
                                   nullptr, y_send, st);
+    return hip_status(e);
+  }
+  const int sp = large_down_splits(s);
+  if (sp > 1) {
+    if (e == hipSuccess)
+      e = launch_grouped_mlp(s, x_recv, w.sorted_slot, w.offsets, w_gate, w_up, w_down, nullptr, nullptr, nullptr,
+                             nullptr, nullptr, w.grouped_ws, st);
+    if (e == hipSuccess)
+      e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), sp, w.pos, nullptr, y_send, st);
     return hip_status(e);
   }
   if (e == hipSuccess)

@@ -59,6 +59,12 @@ size_t grouped_ws_bytes(const Shape& s);
 constexpr int kSmallMMaxRows = 64;
 bool use_small_m(const Shape& s);
 int small_m_splits(const Shape& s, bool gated);
+// K splits of the tiled down launch (1 or 2), from the widths only: a long K against a narrow
+// output leaves few tiles per CU, and the last, partly filled round of tiles then dominates
+int large_down_splits(const Shape& s);
+// y_perm / y_shared from fp32 split partials [splits][max_kept + n_s*T][d], in split order
+hipError_t launch_split_reduce(const Shape& s, const float* part, int splits, const int32_t* offsets, void* y_perm,
+                               void* y_shared, hipStream_t st);
 size_t small_m_ws_bytes(const Shape& s);
 // Launches of the bf16 grouped GEMM (grouped_mlp.hip): out[row][n] = sum_k in[src(row)][k] *
 // w_g[n][k] over tiles of 256 rows x 256 weight rows.
@@ -67,7 +73,8 @@ enum GemmMode {
   kGemmPlain = 1,        // forward down: routed rows read in[row], shared rows in[s*T + t]
   kGemmGatedSave = 2,    // gate/up storing both products, [rows][2N] = (x Wg | x Wu)
   kGemmPlainGather = 3,  // one weight matrix, rows read as the gated launch reads them
-  kGemmWgrad = 4         // weight gradients: fixed M rows per group, K = the group's segment
+  kGemmWgrad = 4,        // weight gradients: fixed M rows per group, K = the group's segment
+  kGemmPlainSplit = 5    // kGemmPlain with K split: fp32 partials [splits][max_kept + n_s*T][N]
 };
 struct GemmLaunch {
   int mode;
@@ -91,6 +98,10 @@ struct GemmLaunch {
   int ld_in_r, ld_w_r, ld_in_s, ld_w_s;
   int64_t in_s_gstride, w_s_gstride;
   int M_r, M_s;
+  // kGemmPlainSplit
+  float* part;
+  int splits;
+  int64_t max_kept;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st);
 // the device tile table of the grouped GEMM (routed groups from offsets, then shared); also

@@ -75,6 +75,11 @@ struct GemmArgs {
   int64_t in_s_gstride, w_s_gstride;  // elements between consecutive shared groups
   int M_r, M_s;                // output rows of a routed / shared group
   int mt_r, mt_s, n_m;         // m-tiles of a routed / shared group, and in all
+  // split-K down launch (kGemmPlainSplit): fp32 partials [splits][part_rows][N], routed rows
+  // first, then shared expert s's token t at max_kept + s*T + t
+  float* part;
+  int splits;
+  int64_t max_kept, part_rows;
 };
 
 // Chunk swizzle of LDS row r (its 16-byte chunk c is stored at slot c ^ swz(r)). It makes
@@ -288,10 +293,10 @@ static_assert(IPW == 8 || BK != 32, "the pipelined loop issues 8 DMA instruction
 // K loop and epilogue of one wave, for LIVE (compile-time) token sub-tiles of 32 rows that
 // hold data. Every wave of a block runs the same number of K steps and barriers; waves
 // with fewer live sub-tiles skip MFMAs, not loads.
-template <bool GATED, int BT, int LIVE, bool SAVE = false>
+template <bool GATED, int BT, int LIVE, bool SAVE = false, bool F32 = false>
 __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K, int wave,
                                           int lane, int row0, int row1, int n0, int N,
-                                          bf16_t* out, int64_t out_row_base) {
+                                          void* out_v, int64_t out_row_base) {
   constexpr int WT = BT / 2;
   constexpr int STAGE = (BW + BT) * BK;  // bf16 elements per stage
   const int wn = wave & 1, wm = wave >> 1;
@@ -378,9 +383,20 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
   for (int j = 0; j < LIVE; ++j) {
     const int row = row0 + tok0 + j * 32 + l32;
     if (row >= row1) continue;
-    // SAVE: the gate and up products themselves, side by side in a row of 2N
-    bf16_t* op = out + (out_row_base + row) * (SAVE ? 2 * N : N);
-    if (GATED && SAVE) {
+    // SAVE: the gate and up products themselves, side by side in a row of 2N; F32: fp32 sums
+    bf16_t* op = static_cast<bf16_t*>(out_v) + (out_row_base + row) * (SAVE ? 2 * N : N);
+    if (!GATED && F32) {
+      float* opf = static_cast<float*>(out_v) + (out_row_base + row) * N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * 128 + i * 32 + q * 8 + khalf * 4;
+          if (n < N)
+            *reinterpret_cast<float4*>(opf + n) =
+                make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+        }
+    } else if (GATED && SAVE) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -447,8 +463,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
   constexpr bool SAVE = MODE == kGemmGatedSave;
   constexpr bool GATHER = GATED || MODE == kGemmPlainGather;
   constexpr bool WGRAD = MODE == kGemmWgrad;
+  constexpr bool SPLIT = MODE == kGemmPlainSplit;
   constexpr int WT = BT / 2;  // token rows per wave
   constexpr int TJ = WT / 32; // token sub-tiles per wave
+  int split = 0;
+  if constexpr (SPLIT) {  // the split is the slowest index: each split sweeps the tiles in raster order
+    const int per = n_m * n_n;
+    split = L / per;
+    L -= split * per;
+  }
   const int in_group = kGroupM * n_n;
   const int first_m = (L / in_group) * kGroupM;
   const int gsz = min(n_m - first_m, kGroupM);
@@ -512,6 +535,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
     in = shared ? a.in_s : a.in_r;
     ldw = K;
     ldin = K;
+    if constexpr (SPLIT) {  // this split's K range; rows keep their full stride
+      const int ks = K / a.splits;
+      w0 += split * ks;
+      in += split * ks;
+      K = ks;
+    }
   }
 
   const int tid = threadIdx.x;
@@ -552,25 +581,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
     }
   }
 
-  bf16_t* out = shared ? a.out_s : a.out_r;
+  void* out = SPLIT ? static_cast<void*>(a.part) : static_cast<void*>(shared ? a.out_s : a.out_r);
   int64_t out_row_base;
   if constexpr (WGRAD)
     out_row_base = static_cast<int64_t>(gi) * (shared ? a.M_s : a.M_r);
+  else if constexpr (SPLIT)
+    out_row_base = split * a.part_rows + (shared ? a.max_kept + static_cast<int64_t>(gi) * a.T : 0);
   else
     out_row_base = shared ? static_cast<int64_t>(gi) * a.T : 0;
   const int valid_rows = row1 - row0 - (wave >> 1) * WT;
   const int live = __builtin_amdgcn_readfirstlane(valid_rows <= 0 ? 0 : min(TJ, (valid_rows + 31) / 32));
   static_assert(TJ == 4 || TJ == 2, "token sub-tiles per wave");
   if (live >= TJ)
-    tile_loop<GATED, BT, TJ, SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, TJ, SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (live == 0)
-    tile_loop<GATED, BT, 0, SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, 0, SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (live == 1)
-    tile_loop<GATED, BT, 1, SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, 1, SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (TJ == 4 && live == 2)
-    tile_loop<GATED, BT, (TJ == 4 ? 2 : 1), SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, (TJ == 4 ? 2 : 1), SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else
-    tile_loop<GATED, BT, (TJ == 4 ? 3 : 1), SAVE>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, (TJ == 4 ? 3 : 1), SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
 }
 
 // Persistent launch: one block per CU takes tiles from queues until all are done. The
@@ -588,7 +619,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
   int* next_tile = reinterpret_cast<int*>(lds + kRing);
   const int n_m = MODE == kGemmWgrad ? a.n_m : *a.n_tiles;
   const int n_n = a.n_tiles_n;
-  const int G = n_m * n_n;
+  const int G = n_m * n_n * (MODE == kGemmPlainSplit ? a.splits : 1);
   const int per_xcd = (G + 7) / 8;
   // XCC_ID hardware register (bits 3:0): the XCD this block runs on
   int xcd = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) & 15;
@@ -767,7 +798,7 @@ struct GroupedWs {
   int32_t* n_tiles;  // [0]: m-tile count; [16, 16 + kQueueInts): tile counters
   void* h;
   void* hs;
-  float* part;  // small-batch path: split-K partials
+  float* part;  // split-K partials: the small-batch launches, or the split tiled down launch
 };
 
 GroupedWs carve(const Shape& s, void* ws) {
@@ -791,11 +822,27 @@ GroupedWs carve(const Shape& s, void* ws) {
 
 float* small_m_partials(const Shape& s, void* ws) { return carve(s, ws).part; }
 
+int large_down_splits(const Shape& s) {
+  if (s.dtype != MOE_BF16 || use_small_m(s)) return 1;
+  auto halves = [](int K) { return K % 128 == 0; };  // each half a multiple of 64
+  if (s.f >= 2 * s.d && halves(s.f) && (s.n_shared == 0 || halves(s.f_s))) return 2;
+  return 1;
+}
+
+// fp32 partials of a split-K down launch (the small-batch path keeps its own there)
+size_t large_split_ws_bytes(const Shape& s) {
+  const int sp = large_down_splits(s);
+  if (sp <= 1) return 0;
+  const int64_t rows_total = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
+  return align256(static_cast<size_t>(sp) * rows_total * s.d * sizeof(float));
+}
+
 size_t grouped_ws_bytes(const Shape& s) {
   const size_t es = s.dtype == MOE_BF16 ? 2 : 4;
   return align256(static_cast<size_t>(m_tile_bound(s)) * kTileEntries * sizeof(int32_t)) + 256 +
          align256(static_cast<size_t>(s.max_kept) * s.f * es) +
-         align256(static_cast<size_t>(s.n_shared) * s.T * s.f_s * es) + small_m_ws_bytes(s);
+         align256(static_cast<size_t>(s.n_shared) * s.T * s.f_s * es) +
+         std::max(small_m_ws_bytes(s), large_split_ws_bytes(s));
 }
 
 // compute units of the current device (cached per device)
@@ -850,6 +897,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st) {
   a.w_s_gstride = L.w_s_gstride;
   a.M_r = L.M_r;
   a.M_s = L.M_s;
+  a.part = L.part;
+  a.splits = L.mode == kGemmPlainSplit ? L.splits : 1;
+  a.max_kept = L.max_kept;
+  a.part_rows = L.max_kept + static_cast<int64_t>(L.n_shared) * L.T;
   const bool gated = L.mode == kGemmGated || L.mode == kGemmGatedSave;
   const int n_max = L.n_shared > 0 && L.N_s > L.N_r ? L.N_s : L.N_r;
   a.n_tiles_n = gated ? (n_max + BW / 2 - 1) / (BW / 2) : (n_max + BW - 1) / BW;
@@ -860,7 +911,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st) {
     a.n_m = L.E * a.mt_r + L.n_shared * (L.n_shared > 0 ? a.mt_s : 0);
     mb = a.n_m;
   }
-  const int64_t grid = std::min<int64_t>(cu_count(), static_cast<int64_t>(a.n_tiles_n) * mb);
+  const int64_t grid = std::min<int64_t>(cu_count(), static_cast<int64_t>(a.n_tiles_n) * mb * a.splits);
   if (grid <= 0) return hipSuccess;
   const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
   switch (L.mode) {
@@ -869,6 +920,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st) {
     case kGemmGatedSave: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGatedSave, kBT>), gd, bd, 0, st, a); break;
     case kGemmPlainGather: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainGather, kBT>), gd, bd, 0, st, a); break;
     case kGemmWgrad: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmWgrad, kBT>), gd, bd, 0, st, a); break;
+    case kGemmPlainSplit: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainSplit, kBT>), gd, bd, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -934,10 +986,23 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.K_s = s.f_s;
     a.n_tiles_n = (s.d + BW - 1) / BW;
     a.queue = queues + 8;
-    const int64_t g2 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb);
+    // a long K against a narrow output: split K in two, fp32 partials reduced in split order
+    // (or summed by the layer's combine when y_perm is null)
+    const int sp = large_down_splits(s);
+    a.splits = sp;
+    a.part = w.part;
+    a.max_kept = s.max_kept;
+    a.part_rows = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
+    const int64_t g2 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb * sp);
     timing_begin(MOE_KERNEL_DOWN, st);
-    hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kBT>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, st, a);
+    if (sp > 1)
+      hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainSplit, kBT>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kBT>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, st,
+                         a);
     timing_end(MOE_KERNEL_DOWN, st);
+    if (sp > 1 && y_perm != nullptr) return launch_split_reduce(s, w.part, sp, offsets, y_perm, y_shared, st);
   } else {
     GemmArgsF32 a{};
     a.sorted_slot = sorted_slot;

@@ -451,6 +451,16 @@ int max_groups(const Shape& s) {
 
 bool use_small_m(const Shape& s) { return s.dtype == MOE_BF16 && s.T <= kSmallMMaxRows; }
 
+hipError_t launch_split_reduce(const Shape& s, const float* part, int splits, const int32_t* offsets, void* y_perm,
+                               void* y_shared, hipStream_t st) {
+  const int64_t rows_total = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
+  const int64_t threads = rows_total * (s.d / 4);
+  hipLaunchKernelGGL(small_m_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st, part,
+                     offsets, s.E, s.max_kept, s.n_shared, static_cast<int>(s.T), s.d, splits,
+                     static_cast<bf16_t*>(y_perm), static_cast<bf16_t*>(y_shared));
+  return hipGetLastError();
+}
+
 // K splits per launch: enough (group, chunk, split) units that the tail of the launch (the
 // last, partly filled round of waves) is short, while each split keeps >= 1024 of K.
 constexpr int64_t kSmallMUnitsTarget = 8192;

@@ -31,6 +31,11 @@ CASES = [
     # small batches through the weight-streaming path, with a shared expert and a K tail
     R(configs.DEEPSEEK_V3, T=40, d_model=320, d_ff=192, n_experts=64, d_ff_shared=320),
     R(configs.QWEN3_FINE_CF, T=57, d_model=256, d_ff=128, n_experts=16, top_k=4),
+    # tiled down launch with K split in two (d_ff >= 2 d_model), ragged tiles, with and
+    # without a shared expert and capacity
+    R(configs.MIXTRAL_PREFILL, T=600, d_model=256, d_ff=768),
+    R(configs.DEEPSEEK_V3, T=300, d_model=128, d_ff=384, n_experts=16, top_k=4, d_ff_shared=256,
+      capacity_factor=1.0),
     # small batches wide enough to split K in both launches (a 64-wide tail inside each split)
     R(configs.mixtral_decode(4), d_model=2176, d_ff=2176),
     R(configs.DEEPSEEK_V3, T=8, d_model=2048, d_ff=2048, n_experts=16, top_k=4, d_ff_shared=2048),
