@@ -136,7 +136,8 @@ class DeviceLayer:
                                    dtype=torch.uint8, device=dev),
             grouped_ws=torch.empty(max(1, binding.moe_workspace_size(cfg, binding.MOE_OP_GROUPED_MLP)),
                                    dtype=torch.uint8, device=dev),
-            y_perm=torch.empty((mk, cfg.d_model), dtype=dt, device=dev),
+            # rows past N_kept (capacity mode) are never written: zeros, not leftovers
+            y_perm=torch.zeros((mk, cfg.d_model), dtype=dt, device=dev),
             y_shared=(torch.empty((cfg.n_shared, cfg.T, cfg.d_model), dtype=dt, device=dev)
                       if cfg.n_shared else None),
             y=torch.empty((cfg.T, cfg.d_model), dtype=dt, device=dev),
