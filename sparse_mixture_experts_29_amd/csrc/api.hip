@@ -91,6 +91,15 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
 
+// K splits of the backward's dx launch (K = 2f, N = d): split while there are fewer than
+// four tiles per CU (the last, partly filled round of long-K tiles otherwise dominates)
+int bwd_dx_splits(const Shape& s) {
+  const int64_t tiles = ((s.d + 255) / 256) * gemm_m_tile_bound(s);
+  int sp = 1;
+  while (sp < 4 && tiles * sp < 1024 && s.f % (64 * sp) == 0 && (s.n_shared == 0 || s.f_s % (64 * sp) == 0)) sp *= 2;
+  return sp;
+}
+
 // Backward workspace: the forward's routing state, the recomputed products, transposed
 // weights, the intermediates of the dgrad chain, and transposed, zero-padded activations
 // for the weight gradients, 256-byte aligned.
@@ -112,6 +121,7 @@ struct BwdWs {
   void *dab, *dab_s, *h, *hs;       // [rows][2f]: da | db;  [rows][f]: h
   float* d_gate;                    // [T*k]
   void* dx_perm;                    // [max_kept][d]
+  float* dxpart;                    // split-K partials of the dx launch
   void* dx_s;                       // [n_s + 1][T][d]: shared experts' dx, then the router's
   float* dl;                        // [T][E]
   float* aux_part;                  // [T]
@@ -163,6 +173,8 @@ BwdWs bwd_layout(const Shape& s, void* base) {
   w.hs = take(ns * T * fs * 2);
   w.d_gate = reinterpret_cast<float*>(take(pairs * 4));
   w.dx_perm = take(mk * d * 2);
+  const int dsp = bwd_dx_splits(s);
+  w.dxpart = reinterpret_cast<float*>(take(dsp > 1 ? dsp * (mk + ns * T) * d * 4 : 0));
   w.dx_s = take((ns + 1) * T * d * 2);
   w.dl = reinterpret_cast<float*>(take(T * E * 4));
   w.aux_part = reinterpret_cast<float*>(take(T * 4));
@@ -586,11 +598,19 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
   L.N_s = d;
   L.K_s = 2 * fs;
   L.queue = w.ctrl + 32;
+  const int dsp = bwd_dx_splits(s);
+  if (dsp > 1) {  // fp32 partials of the K splits, reduced into dx_perm / dx_s in split order
+    L.mode = kGemmPlainSplit;
+    L.splits = dsp;
+    L.part = w.dxpart;
+    L.max_kept = s.max_kept;
+  }
   if (e == hipSuccess) {
     timing_begin(MOE_KERNEL_BWD_GATE_UP_DGRAD, st);
     e = launch_grouped_gemm(L, st);
     timing_end(MOE_KERNEL_BWD_GATE_UP_DGRAD, st);
   }
+  if (e == hipSuccess && dsp > 1) e = launch_split_reduce(s, w.dxpart, dsp, w.offsets, w.dx_perm, w.dx_s, st);
   // (5) router: logit gradients (+ balancing loss), weight, bias and input gradients
   void* dx_router = static_cast<char*>(w.dx_s) + static_cast<size_t>(ns) * s.T * d * 2;
   if (e == hipSuccess)
