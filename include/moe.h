@@ -84,7 +84,9 @@ enum { /* kernels that moe_time_next_launch can bracket */
 /* The problem statement of one layer (the pages' T tokens, d_model, d_ff, E experts,
  * top-k, gating function, capacity factor and shared experts).
  * Limits: 1 <= top_k <= min(E, 32); 1 <= E <= 1024; d_model and d_ff (and d_ff_shared)
- * multiples of 64; T < 2^31 / top_k. capacity_factor <= 0 means dropless; otherwise each
+ * multiples of 64; T < 2^31 / top_k; each activation matrix under 4 GiB: T*d_model,
+ * max_kept*d_ff and n_shared*T*d_ff_shared elements of dtype (MOE_ERR_UNSUPPORTED
+ * otherwise). capacity_factor <= 0 means dropless; otherwise each
  * expert keeps at most C = ceil(capacity_factor * T * top_k / E) (token, expert) pairs,
  * the ones with the lowest token index, evaluated in double precision. */
 typedef struct moe_config {

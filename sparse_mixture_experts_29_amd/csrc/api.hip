@@ -41,6 +41,12 @@ moe_status to_shape(const moe_config* c, Shape* s) {
   }
   const int64_t pairs = c->T * c->top_k;
   s->max_kept = s->capacity < 0 ? pairs : std::min<int64_t>(pairs, s->capacity * c->n_experts);
+  // the tiled GEMMs address rows of one activation matrix (x, h, the shared experts' h)
+  // with 32-bit byte offsets: each must stay under 4 GiB
+  const int64_t lim = int64_t{1} << 32, esz = c->dtype == MOE_BF16 ? 2 : 4;
+  if (s->T * s->d * esz >= lim || s->max_kept * s->f * esz >= lim ||
+      static_cast<int64_t>(s->n_shared) * s->T * s->f_s * esz >= lim)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -87,6 +87,10 @@ def _cfg(**kw):
     (dict(d_ff=96), binding.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=2048, top_k=2), binding.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=64, top_k=33), binding.MOE_ERR_UNSUPPORTED),
+    # activation matrices of 4 GiB and more (32-bit row offsets in the tiled GEMMs)
+    (dict(T=1 << 20, d_model=2048, d_ff=256), binding.MOE_ERR_UNSUPPORTED),
+    (dict(T=(1 << 19) - 1, d_model=4096, d_ff=256), binding.MOE_OK),
+    (dict(T=1 << 18, d_model=256, d_ff=4096, top_k=2), binding.MOE_ERR_UNSUPPORTED),
     (dict(T=0), binding.MOE_OK),
 ])
 def test_config_validation(kw, status):
