@@ -114,6 +114,40 @@ def time_steps(step, K: int, warmup: int, stream, kernel=None):
     return elapsed, step_ms, gate_up_ms
 
 
+def cold_steps(step, K: int, stream, flush_mib: int, mode: str = "read"):
+    """K steps, each after streaming a flush_mib MiB scratch buffer through the caches so that
+    the MALL holds none of the weights; each step timed alone with events around it (the flush
+    is not timed). mode "read" sums the buffer (clean lines only); "write" fills it, which
+    also leaves dirty lines whose write-back then lands inside the step.
+    Returns (per-step ms, per-step ms of the gated launch)."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_29_amd import binding
+    ev = HipEvents()
+    buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda:0")
+    begins = [ev.create() for _ in range(K)]
+    ends = [ev.create() for _ in range(K)]
+    se = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    buf.fill_(1)
+    for i in range(K):
+        if mode == "write":
+            buf.fill_(i & 0xFF)
+        else:
+            buf.sum()
+        se[i][0].record(stream)
+        binding.moe_time_next_launch(binding.MOE_KERNEL_GATE_UP, begins[i], ends[i])
+        step()
+        se[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([a.elapsed_time(b) for a, b in se])
+    gate_ms = np.array([ev.elapsed_ms(begins[i], ends[i]) for i in range(K)])
+    for e in begins + ends:
+        ev.destroy(e)
+    del buf
+    return step_ms, gate_ms
+
+
 def shard_bench(args, w):
     """One GPU's share of an expert-parallel layer: route the whole layer on the GPU, keep
     the rows whose experts this shard owns, and time moe_expert_shard_forward on them."""
@@ -341,6 +375,10 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the training step (forward + moe_layer_backward) of the workload")
     ap.add_argument("--aux-coef", type=float, default=0.01, help="balancing-loss coefficient (--backward)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="also time K cold steps, each after writing this many MiB of scratch (the MALL "
+                         "holds no weights at the step's start); reported under 'cold', not in value")
+    ap.add_argument("--flush-mode", choices=("read", "write"), default="read")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many MiB once (a plain copy "
                          "kernel of known size, to scale the HBM byte counters of a profiler run)")
@@ -466,6 +504,17 @@ def main():
             "max_over_mean_load": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
         },
     }
+    if args.flush_mib:
+        cold_ms, cold_gate = cold_steps(dev.forward, K, stream, args.flush_mib, args.flush_mode)
+        cold = {"flush_mib": args.flush_mib, "flush_mode": args.flush_mode,
+                "ms_per_step": round(float(cold_ms.mean()), 4),
+                "value": round(cfg.T / (cold_ms.mean() * 1e-3), 1),
+                "step_ms_p50": round(float(np.percentile(cold_ms, 50)), 4),
+                "gate_up_avg_ms": round(float(cold_gate.mean()), 4)}
+        if small_batch:
+            cold["gate_up_gbps"] = round(roofline["bytes_per_launch"] / (cold_gate.mean() * 1e-3) / 1e9, 1)
+            cold["layer_hbm_frac"] = round(layer_bytes / (cold_ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        out["cold"] = cold
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(li, min(args.cpu_tokens, cfg.T))
     print(json.dumps(out), flush=True)
