@@ -277,8 +277,10 @@ typedef struct moe_layer_grads {
  * accumulate in fp32 too). Experts that receive no pairs get zero gradients.
  * cfg->dtype must be MOE_BF16 (MOE_ERR_UNSUPPORTED otherwise, and for shapes whose
  * transposed intermediates exceed 4 GiB per matrix). Needs ws of MOE_OP_LAYER_BACKWARD
- * bytes (it holds transposed copies of the expert weights, so it is about the size of the
- * expert weights plus a few activation-sized buffers). T = 0 writes nothing. */
+ * bytes: activation-sized buffers only (the recomputed products, the dgrad intermediates
+ * and transposed activation segments, about 12 * f bytes per kept pair plus a few [T][d]
+ * and [kept][d] matrices); the weights are read as stored, never copied. T = 0 writes
+ * nothing. */
 MOE_API moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
                               const float* router_bias, const void* w_gate, const void* w_up,
                               const void* w_down, const void* ws_gate, const void* ws_up,

@@ -106,9 +106,9 @@ int bwd_dx_splits(const Shape& s) {
   return sp;
 }
 
-// Backward workspace: the forward's routing state, the recomputed products, transposed
-// weights, the intermediates of the dgrad chain, and transposed, zero-padded activations
-// for the weight gradients, 256-byte aligned.
+// Backward workspace: the forward's routing state, the recomputed products, the
+// intermediates of the dgrad chain, and transposed, zero-padded activations for the weight
+// gradients, 256-byte aligned. (The dgrad launches read the weights as stored.)
 struct BwdWs {
   int32_t* idx;
   float* gate;
@@ -122,7 +122,6 @@ struct BwdWs {
   int32_t* tiles;
   int32_t* ctrl;  // [0] m-tile count, [16, 64) counters of the six persistent GEMM launches
   void *ab, *ab_s;                  // [rows][2f]: x Wg | x Wu
-  void *wdT, *wguT, *wdsT, *wgusT;  // [E][f][d], [E][d][2f], shared likewise
   void *u, *u_s;                    // [rows][f]: dy Wd
   void *dab, *dab_s, *h, *hs;       // [rows][2f]: da | db;  [rows][f]: h
   float* d_gate;                    // [T*k]
@@ -167,10 +166,6 @@ BwdWs bwd_layout(const Shape& s, void* base) {
   w.ctrl = reinterpret_cast<int32_t*>(take(64 * 4));
   w.ab = take(mk * 2 * f * 2);
   w.ab_s = take(ns * T * 2 * fs * 2);
-  w.wdT = take(E * f * d * 2);
-  w.wguT = take(E * d * 2 * f * 2);
-  w.wdsT = take(ns * fs * d * 2);
-  w.wgusT = take(ns * d * 2 * fs * 2);
   w.u = take(mk * f * 2);
   w.u_s = take(ns * T * fs * 2);
   w.dab = take(mk * 2 * f * 2);
@@ -528,20 +523,6 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
   if (e == hipSuccess)
     e = launch_permute(s, w.idx, w.counts, w.offsets, w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
   if (e == hipSuccess) e = launch_build_tiles(s, w.offsets, w.tiles, w.ctrl, w.ctrl + 16, st);
-  // transposed weights: Wd^T [E][f][d] and (Wg | Wu)^T [E][d][2f]
-  if (e == hipSuccess) e = launch_transpose_batched(w_down, d, f, int64_t{d} * f, w.wdT, d, 0, int64_t{f} * d, E, st);
-  if (e == hipSuccess)
-    e = launch_transpose_batched(w_gate, f, d, int64_t{f} * d, w.wguT, 2 * f, 0, int64_t{d} * 2 * f, E, st);
-  if (e == hipSuccess)
-    e = launch_transpose_batched(w_up, f, d, int64_t{f} * d, w.wguT, 2 * f, f, int64_t{d} * 2 * f, E, st);
-  if (ns > 0) {
-    if (e == hipSuccess)
-      e = launch_transpose_batched(ws_down, d, fs, int64_t{d} * fs, w.wdsT, d, 0, int64_t{fs} * d, ns, st);
-    if (e == hipSuccess)
-      e = launch_transpose_batched(ws_gate, fs, d, int64_t{fs} * d, w.wgusT, 2 * fs, 0, int64_t{d} * 2 * fs, ns, st);
-    if (e == hipSuccess)
-      e = launch_transpose_batched(ws_up, fs, d, int64_t{fs} * d, w.wgusT, 2 * fs, fs, int64_t{d} * 2 * fs, ns, st);
-  }
   GemmLaunch L{};
   L.tiles = w.tiles;
   L.n_tiles = w.ctrl;
@@ -570,13 +551,15 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
     e = launch_grouped_gemm(L, st);
     timing_end(MOE_KERNEL_BWD_RECOMPUTE, st);
   }
-  // (2) u = dy Wd: the pair's token row of dy against Wd^T
-  L.mode = kGemmPlainGather;
+  // (2) u = dy Wd: the pair's token row of dy against Wd [d][f] as stored (K = d rows)
+  L.mode = kGemmDgradGather;
   L.in_r = L.in_s = dy;
-  L.w0_r = w.wdT;
+  L.w0_r = w_down;
   L.w1_r = nullptr;
-  L.w0_s = w.wdsT;
+  L.w0_s = ws_down;
   L.w1_s = nullptr;
+  L.ksw_r = d;
+  L.ksw_s = d;
   L.out_r = w.u;
   L.out_s = w.u_s;
   L.queue = w.ctrl + 24;
@@ -590,13 +573,17 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
   if (e == hipSuccess)
     e = launch_swiglu_bwd(s, w.ab, w.u, w.ab_s, w.u_s, w.offsets, w.sorted_slot, w.gate, w.dab, w.h, w.dab_s, w.hs,
                           w.d_gate, st);
-  // (4) dx of every pair: (da | db) against (Wg | Wu)^T
-  L.mode = kGemmPlain;
+  // (4) dx of every pair: (da | db) against Wg then Wu, [f][d] each as stored (K = 2f rows)
+  L.mode = kGemmDgrad;
   L.sorted_slot = nullptr;
   L.in_r = w.dab;
   L.in_s = w.dab_s;
-  L.w0_r = w.wguT;
-  L.w0_s = w.wgusT;
+  L.w0_r = w_gate;
+  L.w1_r = w_up;
+  L.w0_s = ws_gate;
+  L.w1_s = ws_up;
+  L.ksw_r = f;
+  L.ksw_s = fs;
   L.out_r = w.dx_perm;
   L.out_s = w.dx_s;
   L.N_r = d;
@@ -606,7 +593,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
   L.queue = w.ctrl + 32;
   const int dsp = bwd_dx_splits(s);
   if (dsp > 1) {  // fp32 partials of the K splits, reduced into dx_perm / dx_s in split order
-    L.mode = kGemmPlainSplit;
+    L.mode = kGemmDgradSplit;
     L.splits = dsp;
     L.part = w.dxpart;
     L.max_kept = s.max_kept;

@@ -18,40 +18,7 @@
 namespace moe {
 namespace {
 
-constexpr int kTile = 64;  // transpose tile (rows x columns)
-
-// dst[b][c][coff + r] = src[b][r][c] for r < R, c < C (R and C multiples of 64).
-__global__ __launch_bounds__(256) void transpose_batched_kernel(const bf16_t* __restrict__ src, int R, int C,
-                                                                int64_t src_bstride, bf16_t* __restrict__ dst,
-                                                                int ldd, int coff, int64_t dst_bstride) {
-  __shared__ bf16_t tile[kTile][kTile + 2];
-  const int c0 = blockIdx.x * kTile, r0 = blockIdx.y * kTile;
-  const bf16_t* s = src + blockIdx.z * src_bstride;
-  bf16_t* d = dst + blockIdx.z * dst_bstride;
-  const int t = threadIdx.x;
-  {  // 64 rows x 64 columns: 4 threads per row, 16 columns (32 bytes) each
-    const int r = t >> 2, cq = (t & 3) * 16;
-    const uint4* p = reinterpret_cast<const uint4*>(s + static_cast<int64_t>(r0 + r) * C + c0 + cq);
-    const uint4 v0 = p[0], v1 = p[1];
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      tile[r][cq + 2 * q] = static_cast<bf16_t>(w[q] & 0xFFFF);
-      tile[r][cq + 2 * q + 1] = static_cast<bf16_t>(w[q] >> 16);
-    }
-  }
-  __syncthreads();
-  {  // output row c (= input column), 16 consecutive r per thread
-    const int c = t >> 2, rq = (t & 3) * 16;
-    uint32_t w[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      w[q] = static_cast<uint32_t>(tile[rq + 2 * q][c]) | (static_cast<uint32_t>(tile[rq + 2 * q + 1][c]) << 16);
-    uint4* p = reinterpret_cast<uint4*>(d + static_cast<int64_t>(c0 + c) * ldd + coff + r0 + rq);
-    p[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    p[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  }
-}
+constexpr int kTile = 64;  // transpose tile of the activation segments (rows x columns)
 
 // poff[e] = sum over e' < e of kept rows of e' rounded up to 64 (one block, E <= 1024).
 __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
@@ -438,15 +405,6 @@ __global__ __launch_bounds__(256) void fill_kernel(uint32_t* __restrict__ p, int
 unsigned blocks(int64_t n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
 
 }  // namespace
-
-hipError_t launch_transpose_batched(const void* src, int R, int C, int64_t src_bstride, void* dst, int ldd, int coff,
-                                    int64_t dst_bstride, int batch, hipStream_t st) {
-  if (batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_batched_kernel, dim3(C / kTile, R / kTile, batch), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(src), R, C, src_bstride, static_cast<bf16_t*>(dst), ldd, coff,
-                     dst_bstride);
-  return hipGetLastError();
-}
 
 hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st) {
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, E, poff);

@@ -72,9 +72,11 @@ enum GemmMode {
   kGemmGated = 0,        // forward gate/up with the SiLU*mul epilogue: h [rows][N]
   kGemmPlain = 1,        // forward down: routed rows read in[row], shared rows in[s*T + t]
   kGemmGatedSave = 2,    // gate/up storing both products, [rows][2N] = (x Wg | x Wu)
-  kGemmPlainGather = 3,  // one weight matrix, rows read as the gated launch reads them
+  kGemmDgradGather = 3,  // one weight matrix stored [K][N], rows read as the gated launch reads them
   kGemmWgrad = 4,        // weight gradients: fixed M rows per group, K = the group's segment
-  kGemmPlainSplit = 5    // kGemmPlain with K split: fp32 partials [splits][max_kept + n_s*T][N]
+  kGemmPlainSplit = 5,   // kGemmPlain with K split: fp32 partials [splits][max_kept + n_s*T][N]
+  kGemmDgrad = 6,        // kGemmPlain rows against weights stored [K][N]: w0 [ksw][N] then w1 [K-ksw][N]
+  kGemmDgradSplit = 7    // kGemmDgrad with K split, partials as kGemmPlainSplit
 };
 struct GemmLaunch {
   int mode;
@@ -98,10 +100,13 @@ struct GemmLaunch {
   int ld_in_r, ld_w_r, ld_in_s, ld_w_s;
   int64_t in_s_gstride, w_s_gstride;
   int M_r, M_s;
-  // kGemmPlainSplit
+  // kGemmPlainSplit, kGemmDgradSplit
   float* part;
   int splits;
   int64_t max_kept;
+  // dgrad modes (weights stored [K][N], read along their output index): the first ksw rows
+  // of K come from w0 ([E][ksw][N]), the rest from w1 ([E][K-ksw][N]); ksw = K for one matrix
+  int ksw_r, ksw_s;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st);
 // the device tile table of the grouped GEMM (routed groups from offsets, then shared); also
@@ -152,10 +157,7 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
 hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos,
                           const float* gate, const void* y_shared, void* y, hipStream_t st);
 
-// Per-host-thread request of moe_time_next_launch.
 // Backward pass (backward.hip).
-hipError_t launch_transpose_batched(const void* src, int R, int C, int64_t src_bstride, void* dst, int ldd, int coff,
-                                    int64_t dst_bstride, int batch, hipStream_t st);
 hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
 hipError_t launch_transpose_segments(const void* src, int src_ld, int64_t src_bstride, const int32_t* off,
                                      const int32_t* poff, int nseg, int len1, int64_t padded_rows_bound,

@@ -80,6 +80,9 @@ struct GemmArgs {
   float* part;
   int splits;
   int64_t max_kept, part_rows;
+  // dgrad modes: weights stored [K][N]; K rows 0..ksw-1 from w0 [E][ksw][N], the rest from
+  // w1 [E][K-ksw][N]
+  int ksw_r, ksw_s;
 };
 
 // Chunk swizzle of LDS row r (its 16-byte chunk c is stored at slot c ^ swz(r)). It makes
@@ -91,6 +94,43 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Weights stored [K][N] (the dgrad modes): a stage's weight part is BK rows of k by BW
+// columns (512 B per row), 64-byte segment s of row r stored at segment s ^ tr_swz(r). A
+// transposing read of a 32 x 16 operand fragment touches rows k0+{0..3} (lanes 0-31) and
+// k0+{8..11} (lanes 32-63) at one segment: tr_swz sends those 8 rows to 8 distinct segments.
+__device__ __forceinline__ int tr_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Direct-to-LDS 16-byte load (lane l's 16 bytes at g land at LDS byte address M0 + 16*l)
+// issued from assembly, for the launches that read weights with ds_read_b64_tr_b16. The
+// compiler's wait insertion assumes that such a read may alias any LDS DMA in flight (the
+// intrinsic carries no alias information) and would drain the whole DMA ring before each
+// one; hidden from it, the DMA is ordered by the K loop's own vmcnt waits and barriers,
+// which are what order the plain operand reads against the DMA in every mode. The
+// instruction has no register result; M0 is written here and declared clobbered, one wait
+// state between the write and the load that reads it.
+__device__ __forceinline__ void dma16_untracked(const char* g, const bf16_t* lds_dst) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(lds_dst))));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m0v) : "memory", "m0");
+}
+
+// MFMA operand fragment (column c of the fragment = lane % 32, k = 8 * (lane / 32) + 0..7)
+// of a [K][N] weight stage, from p = the lane's element offset for k rows +0..3: two
+// ds_read_b64_tr_b16, each of which hands lane i of a 16-lane group element i % 4 of the
+// 8 bytes addressed by lane 4j + i / 4 as its element j. Lane 4j + q of a group therefore
+// addresses row j, columns 4q..4q+3 of the group's 16 columns, and receives its column's
+// 4 rows.
+__device__ __forceinline__ bf16x8 read_tr_fragment(const bf16_t* p) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * BW));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 // s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maximum (gfx9 encoding).
 template <int N>
@@ -115,14 +155,32 @@ __device__ __forceinline__ void stage_barrier() {
 // Instruction i of a wave fills its rows RPI*i .. RPI*i+RPI-1: lane l stores chunk slot
 // l%CH of row RPI*i + l/CH, i.e. the row's logical chunk (l%CH) ^ swz(row).
 // Offsets are 32-bit byte offsets from a wave-uniform base.
+// Weights stored [K][N] (TR): weight wave w fills rows w*BK/2 .. w*BK/2 + BK/2 - 1 of the
+// stage, two 512-byte rows per instruction, and a stage's rows are K rows of the matrix, so
+// the per-stage advance is a whole row block (step) and the dx launch switches from the gate
+// to the up matrix at stage sw.
 struct DmaPlan {
   const char* base;   // wave-uniform
   uint32_t off[IPW];  // byte offset of this lane's chunk for instruction i (K offset 0)
+  const char* base1;  // TR: matrix read from stage sw on
+  int64_t step;       // TR: bytes per stage
+  int sw;             // TR: first stage read from base1
 
-  template <int BT>
+  // TR: start of stage st's rows (token waves: step = BK * 2, sw never reached)
+  __device__ __forceinline__ const char* at(int st) const {
+    return st < sw ? base + st * step : base1 + (st - sw) * step;
+  }
+
+  template <int BT, bool TR = false>
   __device__ __forceinline__ void issue(bf16_t* stage, int k0, int wave) const {
+    static_assert(!TR || BT == 256, "TR plans fill whole stages");
     const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
-    if (BT == 256 || wave < 2) {
+    if (TR) {
+      const char* b = at(k0 / BK);
+      bf16_t* dst = stage + wave * 128 * BK;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) dma16_untracked(b + off[i], dst + i * RPI * BK);
+    } else if (BT == 256 || wave < 2) {
       bf16_t* dst = stage + wave * 128 * BK;
 #pragma unroll
       for (int i = 0; i < IPW; ++i)
@@ -163,7 +221,9 @@ __device__ __forceinline__ void wait_stages_in_flight(int later) {
 // reads of stage kt before the DMA that reuses its slot, and (ii) every wave's DMA of stage
 // kt+1 before the reads of C. All waves of a block pass the same number of barriers (one
 // per stage) whatever their LIVE, so waves of a ragged tile stay in step.
-template <int LIVE>
+// TR: the weight operands come from a [K][N] stage through transposing reads (two per
+// fragment, aoff = the lane's offsets of k-step 0), and the DMA addresses stage by stage.
+template <int LIVE, bool TR = false>
 __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE : 1], bf16_t* lds,
                                                 const DmaPlan& dp, int K, int wave,
                                                 const int (&aoff)[4], const int (&boff)[LIVE > 0 ? LIVE : 1],
@@ -178,7 +238,9 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE
   bf16x8 fa0[4], fb0[NB], fa1[4], fb1[NB];
   auto rd = [&](const bf16_t* st, int kk, int idx, bf16x8 (&fa)[4], bf16x8 (&fb)[NB]) {
     const int c = ((kk * 2 + khalf) ^ swz_l) << 3;
-    if (idx < 4)
+    if (TR && idx < 4)
+      fa[idx] = read_tr_fragment(st + aoff[idx] + kk * 16 * BW);
+    else if (idx < 4)
       fa[idx] = *reinterpret_cast<const bf16x8*>(st + aoff[idx] + c);
     else
       fb[idx - 4] = *reinterpret_cast<const bf16x8*>(st + boff[idx - 4] + c);
@@ -191,15 +253,19 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE
   // DMA instruction i of stage `st` (its slot is st % NST)
   auto dma = [&](int st, int i) {
     bf16_t* dst = lds + (st % NST) * STAGE + wave * 128 * BK;
-    const uint32_t kb = static_cast<uint32_t>(st) * BK * 2u;
-    __builtin_amdgcn_global_load_lds(dp.base + dp.off[i] + kb, (lds_void*)(dst + i * RPI * BK), 16, 0, 0);
+    if constexpr (TR) {
+      dma16_untracked(dp.at(st) + dp.off[i], dst + i * RPI * BK);
+    } else {
+      const uint32_t kb = static_cast<uint32_t>(st) * BK * 2u;
+      __builtin_amdgcn_global_load_lds(dp.base + dp.off[i] + kb, (lds_void*)(dst + i * RPI * BK), 16, 0, 0);
+    }
   };
 
   // prologue: stages 0..NST-2 in flight, wait for stage 0, fetch its k-step 0 operands,
   // then the early part of stage NST-1 (its slot has never been used)
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < KT) dp.issue<256>(lds + s * STAGE, s * BK, wave);
+    if (s < KT) dp.issue<256, TR>(lds + s * STAGE, s * BK, wave);
   wait_stages_in_flight(min(NST - 2, KT - 1));
   stage_barrier();
 #pragma unroll
@@ -293,7 +359,7 @@ static_assert(IPW == 8 || BK != 32, "the pipelined loop issues 8 DMA instruction
 // K loop and epilogue of one wave, for LIVE (compile-time) token sub-tiles of 32 rows that
 // hold data. Every wave of a block runs the same number of K steps and barriers; waves
 // with fewer live sub-tiles skip MFMAs, not loads.
-template <bool GATED, int BT, int LIVE, bool SAVE = false, bool F32 = false>
+template <bool GATED, int BT, int LIVE, bool SAVE = false, bool F32 = false, bool TR = false>
 __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K, int wave,
                                           int lane, int row0, int row1, int n0, int N,
                                           void* out_v, int64_t out_row_base) {
@@ -305,9 +371,19 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
   const int swz_l = swz(l32);  // every row a lane reads is l32 + a multiple of 32
   // LDS element offsets of this lane's operand rows
   int aoff[4], boff[LIVE > 0 ? LIVE : 1];
+  static_assert(!(TR && GATED), "the [K][N] weight layout is read by the plain modes only");
+  if constexpr (TR) {
+    // transposing reads of the [K][N] stage: lane 4j + q of 16-lane group g addresses row
+    // 8*khalf + j (+4 for the second read), columns 16*(g & 1) + 4q.. of the fragment
+    const int j = (lane & 15) >> 2, q = lane & 3, hh = (lane >> 4) & 1;
+    const int fl = tr_swz(8 * khalf + j);  // the same for every row this lane reads
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    aoff[i] = ((GATED ? (i < 2 ? 0 : BW / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32) + l32) * BK;
+    for (int i = 0; i < 4; ++i) aoff[i] = (8 * khalf + j) * BW + (((wn * 4 + i) ^ fl) << 5) + 16 * hh + 4 * q;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      aoff[i] = ((GATED ? (i < 2 ? 0 : BW / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32) + l32) * BK;
+  }
 #pragma unroll
   for (int j = 0; j < LIVE; ++j) boff[j] = (BW + tok0 + j * 32 + l32) * BK;
 
@@ -323,7 +399,8 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
   auto fetch = [&](const bf16_t* stage, int kk, bf16x8 (&af)[4], bf16x8 (&bf)[NB]) {
     const int c = ((kk * 2 + khalf) ^ swz_l) << 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(stage + aoff[i] + c);
+    for (int i = 0; i < 4; ++i)
+      af[i] = TR ? read_tr_fragment(stage + aoff[i] + kk * 16 * BW) : *reinterpret_cast<const bf16x8*>(stage + aoff[i] + c);
 #pragma unroll
     for (int j = 0; j < LIVE; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(stage + boff[j] + c);
   };
@@ -353,7 +430,7 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
   static_assert(BK == 64 || BK == 32, "compute() walks 2 or 4 k-steps of 16");
 
   if constexpr (BT == 256 && BK == 32 && NST >= 3) {
-    kloop_pipelined<LIVE>(acc, lds, dp, K, wave, aoff, boff, swz_l, khalf);
+    kloop_pipelined<LIVE, TR>(acc, lds, dp, K, wave, aoff, boff, swz_l, khalf);
   } else {
     // Ring of NST LDS stages, DMA running NST-1 stages ahead of the MFMAs. At step kt the
     // stage kt is complete once at most (NST-2) later stages of DMA are still in flight.
@@ -361,7 +438,7 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
     const int KT = K / BK;
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
-      if (s < KT) dp.issue<BT>(lds + s * STAGE, s * BK, wave);
+      if (s < KT) dp.issue<BT, TR>(lds + s * STAGE, s * BK, wave);
     for (int kt = 0; kt < KT; ++kt) {
       // DMA instructions per stage: IPW, or IPW*BT/256 for token waves of a BT < 256 tile
       if (kt + NST - 2 >= KT)
@@ -372,7 +449,7 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
         wait_vmcnt<(NST - 2) * IPW * BT / 256>();
       stage_barrier();
       const int nxt = kt + NST - 1;
-      if (nxt < KT) dp.issue<BT>(lds + (nxt % NST) * STAGE, nxt * BK, wave);
+      if (nxt < KT) dp.issue<BT, TR>(lds + (nxt % NST) * STAGE, nxt * BK, wave);
       compute(lds + (kt % NST) * STAGE);
     }
   }
@@ -454,16 +531,19 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
 // tile's index in raster order: groups of kGroupM m-tiles sweep every n-tile, so a weight
 // tile is read by kGroupM m-tiles close together in time.
 // MODE (GemmMode): the forward launches (gated with the SiLU*mul epilogue; plain), the
-// gated launch storing both products (kGemmGatedSave), a plain launch whose routed rows
-// gather the input by sorted_slot as the gated launch does (kGemmPlainGather), and the
-// weight-gradient launch (kGemmWgrad, fixed M rows per group, K = the group's segment).
+// gated launch storing both products (kGemmGatedSave), the weight-gradient launch
+// (kGemmWgrad, fixed M rows per group, K = the group's segment), and the dgrad launches,
+// whose weights are stored [K][N] (the forward's matrices read along their output index,
+// no transposed copy): kGemmDgradGather gathers its routed rows by sorted_slot as the gated
+// launch does, kGemmDgrad / kGemmDgradSplit read rows as kGemmPlain does.
 template <int MODE, int BT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L, int n_m, int n_n) {
   constexpr bool GATED = MODE == kGemmGated || MODE == kGemmGatedSave;
   constexpr bool SAVE = MODE == kGemmGatedSave;
-  constexpr bool GATHER = GATED || MODE == kGemmPlainGather;
+  constexpr bool GATHER = GATED || MODE == kGemmDgradGather;
   constexpr bool WGRAD = MODE == kGemmWgrad;
-  constexpr bool SPLIT = MODE == kGemmPlainSplit;
+  constexpr bool SPLIT = MODE == kGemmPlainSplit || MODE == kGemmDgradSplit;
+  constexpr bool TR = MODE == kGemmDgradGather || MODE == kGemmDgrad || MODE == kGemmDgradSplit;
   constexpr int WT = BT / 2;  // token rows per wave
   constexpr int TJ = WT / 32; // token sub-tiles per wave
   int split = 0;
@@ -506,6 +586,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
   if (n0 >= N) return;
   const int gi = shared ? g - a.E : g;
   int K, ldw, ldin;
+  int kstart = 0, ksw = 0;  // TR: first K row of this launch's range, first row of w1
   const bf16_t* w0;
   const bf16_t* w1 = nullptr;
   const bf16_t* in;
@@ -527,6 +608,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
       in = a.in_r + k0;
       ldw = lw_r;
       ldin = li_r;
+    }
+  } else if constexpr (TR) {
+    // this group's matrices: w0 [ksw][N], w1 [K-ksw][N]; rows of K are rows of memory
+    int ksw_r = a.ksw_r, ksw_s = a.ksw_s;
+    asm volatile("" : "+s"(ksw_r), "+s"(ksw_s));
+    K = shared ? a.K_s : a.K_r;
+    ksw = shared ? ksw_s : ksw_r;
+    w0 = (shared ? a.w0_s : a.w0_r) + static_cast<int64_t>(gi) * ksw * N;
+    w1 = (shared ? a.w1_s : a.w1_r) + static_cast<int64_t>(gi) * (K - ksw) * N;
+    in = shared ? a.in_s : a.in_r;
+    ldw = N;
+    ldin = K;
+    if constexpr (SPLIT) {
+      const int ks = K / a.splits;
+      kstart = split * ks;
+      in += kstart;
+      K = ks;
     }
   } else {
     K = shared ? a.K_s : a.K_r;
@@ -550,7 +648,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
   // end (weights past N, tokens past row1) re-read a valid row; their results are dropped.
   DmaPlan dp;
   const int lrow = lane / CH;  // row within an instruction's RPI rows
-  if (wave < 2) {
+  if (TR) {  // token waves advance BK columns a stage and never switch matrices
+    dp.step = BK * 2;
+    dp.sw = 0x7fffffff;
+    dp.base1 = nullptr;
+  }
+  if (TR && wave < 2) {
+    // [K][N] weights: instruction i of weight wave w fills stage rows R = w*BK/2 + 2i + lane/32
+    // (K rows kstart + st*BK + R), 16-byte slot lane%32 of the row, i.e. columns
+    // n0 + 32*((slot/4) ^ tr_swz(R)) + 8*(slot%4). Columns past N re-read column N-8.
+    const int sl = lane & 31;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = wave * (BK / 2) + 2 * i + (lane >> 5);
+      const int col = min(n0 + (((sl >> 2) ^ tr_swz(r)) << 5) + ((sl & 3) << 3), N - 8);
+      dp.off[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(ldw) * 2u + static_cast<uint32_t>(col) * 2u;
+    }
+    dp.step = static_cast<int64_t>(BK) * ldw * 2;
+    if (kstart >= ksw) {  // the whole range lies in w1
+      dp.base = reinterpret_cast<const char*>(w1 + static_cast<int64_t>(kstart - ksw) * ldw);
+      dp.sw = 0x7fffffff;
+    } else {
+      dp.base = reinterpret_cast<const char*>(w0 + static_cast<int64_t>(kstart) * ldw);
+      dp.base1 = reinterpret_cast<const char*>(w1);
+      dp.sw = (ksw - kstart) / BK;
+    }
+  } else if (wave < 2) {
     // gated: wave 0 the 128 gate rows, wave 1 the 128 up rows; else 128 rows each
     const bf16_t* wb = GATED ? (wave == 0 ? w0 : w1) : w0;
     const int nbase = GATED ? n0 : n0 + wave * 128;
@@ -593,15 +716,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
   const int live = __builtin_amdgcn_readfirstlane(valid_rows <= 0 ? 0 : min(TJ, (valid_rows + 31) / 32));
   static_assert(TJ == 4 || TJ == 2, "token sub-tiles per wave");
   if (live >= TJ)
-    tile_loop<GATED, BT, TJ, SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, TJ, SAVE, SPLIT, TR>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (live == 0)
-    tile_loop<GATED, BT, 0, SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, 0, SAVE, SPLIT, TR>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (live == 1)
-    tile_loop<GATED, BT, 1, SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, 1, SAVE, SPLIT, TR>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (TJ == 4 && live == 2)
-    tile_loop<GATED, BT, (TJ == 4 ? 2 : 1), SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, (TJ == 4 ? 2 : 1), SAVE, SPLIT, TR>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else
-    tile_loop<GATED, BT, (TJ == 4 ? 3 : 1), SAVE, SPLIT>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
+    tile_loop<GATED, BT, (TJ == 4 ? 3 : 1), SAVE, SPLIT, TR>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
 }
 
 // Persistent launch: one block per CU takes tiles from queues until all are done. The
@@ -619,7 +742,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(GemmArgs a) {
   int* next_tile = reinterpret_cast<int*>(lds + kRing);
   const int n_m = MODE == kGemmWgrad ? a.n_m : *a.n_tiles;
   const int n_n = a.n_tiles_n;
-  const int G = n_m * n_n * (MODE == kGemmPlainSplit ? a.splits : 1);
+  const int G = n_m * n_n * (MODE == kGemmPlainSplit || MODE == kGemmDgradSplit ? a.splits : 1);
   const int per_xcd = (G + 7) / 8;
   // XCC_ID hardware register (bits 3:0): the XCD this block runs on
   int xcd = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) & 15;
@@ -898,7 +1021,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st) {
   a.M_r = L.M_r;
   a.M_s = L.M_s;
   a.part = L.part;
-  a.splits = L.mode == kGemmPlainSplit ? L.splits : 1;
+  const bool split = L.mode == kGemmPlainSplit || L.mode == kGemmDgradSplit;
+  a.splits = split ? L.splits : 1;
+  a.ksw_r = L.ksw_r;
+  a.ksw_s = L.ksw_s;
   a.max_kept = L.max_kept;
   a.part_rows = L.max_kept + static_cast<int64_t>(L.n_shared) * L.T;
   const bool gated = L.mode == kGemmGated || L.mode == kGemmGatedSave;
@@ -918,9 +1044,11 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st) {
     case kGemmGated: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGated, kBT>), gd, bd, 0, st, a); break;
     case kGemmPlain: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kBT>), gd, bd, 0, st, a); break;
     case kGemmGatedSave: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGatedSave, kBT>), gd, bd, 0, st, a); break;
-    case kGemmPlainGather: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainGather, kBT>), gd, bd, 0, st, a); break;
+    case kGemmDgradGather: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmDgradGather, kBT>), gd, bd, 0, st, a); break;
     case kGemmWgrad: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmWgrad, kBT>), gd, bd, 0, st, a); break;
     case kGemmPlainSplit: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainSplit, kBT>), gd, bd, 0, st, a); break;
+    case kGemmDgrad: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmDgrad, kBT>), gd, bd, 0, st, a); break;
+    case kGemmDgradSplit: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmDgradSplit, kBT>), gd, bd, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -268,7 +268,10 @@ def test_backward_workspace_sizes():
     for cfg in (configs.MIXTRAL_PREFILL, configs.QWEN3_FINE, configs.DEEPSEEK_V3):
         b = binding.moe_workspace_size(cfg, binding.MOE_OP_LAYER_BACKWARD)
         assert b % 256 == 0
-        # holds at least the transposed expert weights
-        assert b >= cfg.n_experts * 3 * cfg.d_model * cfg.d_ff * 2
+        # holds the recomputed x Wg | x Wu, u, da | db and h of every pair (12 f bytes a pair)
+        assert b >= cfg.T * cfg.top_k * 12 * cfg.d_ff
+    # and no copy of the expert weights: the dgrad launches read them as stored
+    ds = configs.DEEPSEEK_V3
+    assert binding.moe_workspace_size(ds, binding.MOE_OP_LAYER_BACKWARD) < ds.n_experts * 3 * ds.d_model * ds.d_ff * 2
     with pytest.raises(binding.MoeError):
         binding.moe_workspace_size(configs.TINY_FP32, binding.MOE_OP_LAYER_BACKWARD)
