@@ -363,11 +363,11 @@ template <bool GATED, int BT, int LIVE, bool SAVE = false, bool F32 = false, boo
 __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K, int wave,
                                           int lane, int row0, int row1, int n0, int N,
                                           void* out_v, int64_t out_row_base) {
-  constexpr int WT = BT / 2;
   constexpr int STAGE = (BW + BT) * BK;  // bf16 elements per stage
   const int wn = wave & 1, wm = wave >> 1;
   const int l32 = lane & 31, khalf = lane >> 5;
-  const int tok0 = wm * WT;
+  // token sub-tile j of this wave = 32-row sub-tile 2j + wm of the tile: the two wave pairs
+  // alternate, so a partly filled tile splits its live rows between them
   const int swz_l = swz(l32);  // every row a lane reads is l32 + a multiple of 32
   // LDS element offsets of this lane's operand rows
   int aoff[4], boff[LIVE > 0 ? LIVE : 1];
@@ -385,7 +385,7 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
       aoff[i] = ((GATED ? (i < 2 ? 0 : BW / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32) + l32) * BK;
   }
 #pragma unroll
-  for (int j = 0; j < LIVE; ++j) boff[j] = (BW + tok0 + j * 32 + l32) * BK;
+  for (int j = 0; j < LIVE; ++j) boff[j] = (BW + (2 * j + wm) * 32 + l32) * BK;
 
   f32x16 acc[4][LIVE > 0 ? LIVE : 1];
 #pragma unroll
@@ -455,10 +455,10 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
   }
 
   // epilogue. acc[i][j] register r of lane l: weight row (operand A) 8*(r/4) + 4*(l/32) + r%4
-  // of sub-tile i, token row tok0 + 32*j + l%32.
+  // of sub-tile i, token row 32*(2j + wm) + l%32.
 #pragma unroll
   for (int j = 0; j < LIVE; ++j) {
-    const int row = row0 + tok0 + j * 32 + l32;
+    const int row = row0 + (2 * j + wm) * 32 + l32;
     if (row >= row1) continue;
     // SAVE: the gate and up products themselves, side by side in a row of 2N; F32: fp32 sums
     bf16_t* op = static_cast<bf16_t*>(out_v) + (out_row_base + row) * (SAVE ? 2 * N : N);
@@ -527,7 +527,8 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
 }
 
 // One tile: BW weight rows x BT token rows, 4 waves as 2 (weights) x 2 (tokens), each
-// wave 128 weight rows x BT/2 tokens of v_mfma_f32_32x32x16_bf16 accumulators. L is the
+// wave 128 weight rows x BT/2 tokens (alternate 32-row sub-tiles) of
+// v_mfma_f32_32x32x16_bf16 accumulators. L is the
 // tile's index in raster order: groups of kGroupM m-tiles sweep every n-tile, so a weight
 // tile is read by kGroupM m-tiles close together in time.
 // MODE (GemmMode): the forward launches (gated with the SiLU*mul epilogue; plain), the
@@ -712,8 +713,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
     out_row_base = split * a.part_rows + (shared ? a.max_kept + static_cast<int64_t>(gi) * a.T : 0);
   else
     out_row_base = shared ? static_cast<int64_t>(gi) * a.T : 0;
-  const int valid_rows = row1 - row0 - (wave >> 1) * WT;
-  const int live = __builtin_amdgcn_readfirstlane(valid_rows <= 0 ? 0 : min(TJ, (valid_rows + 31) / 32));
+  // live token sub-tiles of this wave: those of the tile's ceil(rows/32) that are 2j + wm
+  const int sub = (row1 - row0 + 31) / 32;
+  const int live = __builtin_amdgcn_readfirstlane(max(0, min(TJ, (sub - (wave >> 1) + 1) / 2)));
   static_assert(TJ == 4 || TJ == 2, "token sub-tiles per wave");
   if (live >= TJ)
     tile_loop<GATED, BT, TJ, SAVE, SPLIT, TR>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
