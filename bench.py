@@ -11,7 +11,8 @@ d=4096, f=14336, E=8, top-2, bf16). Prints ONE JSON line (rank 0):
              (4 d f N_kept) / its average launch time, HIP events recorded around that
              launch on the layer's stream inside the timed steps, against 2.5 PFLOP/s
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
-Decode workloads (T <= 64) take the weight-streaming kernels, which are HBM-bound: there the
+Decode workloads (T <= 64) are bound by the touched experts' weight bytes (the weight-streaming
+kernels; bf16 batches averaging 8 or more rows per expert take the tiled GEMM): there the
 roofline is the gated launch's algorithmic bytes (touched experts' gate and up weights as
 stored, token rows in, h out) per launch time, against 8 TB/s. The mixtral_decode_fp8_*
 workloads run the same layer with FP8 E4M3 expert weights (moe_layer_forward_fp8).
@@ -30,7 +31,14 @@ sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-SMALL_BATCH_TOKENS = 64  # bf16 batches up to this size take the weight-streaming kernels
+SMALL_BATCH_TOKENS = 64  # decode batches: up to this size the step is bound by the weight bytes
+SMALL_ROWS_PER_EXPERT = 8  # bf16 decode batches with T*k < 8*E take the weight-streaming kernels
+
+
+def weight_streaming(T: int, k: int, E: int, fp8: bool) -> bool:
+    """Whether the library runs a decode batch on its weight-streaming kernels (FP8 weights
+    always; bf16 while the experts average fewer than 8 rows) rather than the tiled GEMM."""
+    return T <= SMALL_BATCH_TOKENS and (fp8 or T * k < SMALL_ROWS_PER_EXPERT * E)
 METRIC = "routed tokens/sec per MoE layer; % of bf16 MFMA peak (prefill) / HBM peak (decode)"
 
 
@@ -183,7 +191,9 @@ def shard_bench(args, w):
         touched = int((loads > 0).sum())
         bytes_gate_up = float(touched * cfg.gate_up_bytes(cfg.d_ff)) + R * cfg.d_model * es + R * cfg.d_ff * es
         achieved = bytes_gate_up / (gate_up_ms.mean() * 1e-3) / 1e9
-        roofline = {"kernel": "small_m_kernel<gated> (weight-streaming gate/up + SiLU*mul)", "bound": "hbm",
+        kname = ("small_m_kernel<gated> (weight-streaming gate/up + SiLU*mul)"
+                 if weight_streaming(R, 1, per, False) else "grouped_gemm_bf16<gated> (gate/up GEMM + SiLU*mul)")
+        roofline = {"kernel": kname, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                     "avg_launch_ms": round(float(gate_up_ms.mean()), 4), "bytes_per_launch": bytes_gate_up}
@@ -436,23 +446,26 @@ def main():
     es = 2 if cfg.dtype == "bf16" else 4
     small_batch = cfg.dtype == "bf16" and cfg.T <= SMALL_BATCH_TOKENS
     if small_batch:
-        # weight-streaming path: HBM-bound; algorithmic bytes of the gated launch = the touched
-        # experts' gate and up weights as stored (+ shared; FP8: codes and row scales), the
-        # token rows read, the h rows written
+        # decode batch: HBM-bound on either path; algorithmic bytes of the gated launch = the
+        # touched experts' gate and up weights as stored (+ shared; FP8: codes and row scales),
+        # the token rows read, the h rows written
         bytes_gate_up = (float(touched * cfg.gate_up_bytes(cfg.d_ff))
                          + cfg.n_shared * cfg.gate_up_bytes(cfg.d_ff_shared)
                          + cfg.T * cfg.d_model * es + n_kept * cfg.d_ff * es
                          + cfg.n_shared * cfg.T * cfg.d_ff_shared * es)
         achieved = bytes_gate_up / (gate_up_ms.mean() * 1e-3) / 1e9
         roofline = {
-            "kernel": ("small_m_kernel<gated, fp8>" if cfg.fp8 else "small_m_kernel<gated>")
-            + " (weight-streaming gate/up + SiLU*mul)",
+            "kernel": (("small_m_kernel<gated, fp8>" if cfg.fp8 else "small_m_kernel<gated>")
+                       + " (weight-streaming gate/up + SiLU*mul)")
+            if weight_streaming(cfg.T, cfg.top_k, cfg.n_experts, cfg.fp8)
+            else "grouped_gemm_bf16<gated> (tiled gate/up GEMM + SiLU*mul, weight-bound at this batch)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_from_profile("grouped_mlp_small.hip", cfg.name),
+            "traffic": traffic_from_profile("grouped_mlp_small.hip" if weight_streaming(
+                cfg.T, cfg.top_k, cfg.n_experts, cfg.fp8) else "grouped_mlp.hip", cfg.name),
             "avg_launch_ms": round(float(gate_up_ms.mean()), 4),
             "bytes_per_launch": bytes_gate_up,
         }

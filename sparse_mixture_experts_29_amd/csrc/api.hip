@@ -220,7 +220,7 @@ moe_status check_fp8(const moe_fp8_weights* w) {
 // valid weight structs (the shared one only when there are shared experts)
 moe_status fp8_args(const Shape& s, const moe_fp8_weights* experts, const moe_fp8_weights* shared,
                     Fp8Scales* sc) {
-  if (s.dtype != MOE_BF16 || !use_small_m(s)) return MOE_ERR_UNSUPPORTED;
+  if (s.dtype != MOE_BF16 || !small_m_fits(s)) return MOE_ERR_UNSUPPORTED;
   moe_status r = check_fp8(experts);
   if (r == MOE_OK && s.n_shared > 0) r = check_fp8(shared);
   if (r != MOE_OK) return r;
@@ -450,7 +450,7 @@ moe_status moe_grouped_mlp_fp8(const moe_config* cfg, const void* x, const int32
   Shape s;
   moe_status r = to_shape(cfg, &s);
   if (r != MOE_OK) return r;
-  if (s.dtype != MOE_BF16 || !use_small_m(s)) return MOE_ERR_UNSUPPORTED;
+  if (s.dtype != MOE_BF16 || !small_m_fits(s)) return MOE_ERR_UNSUPPORTED;
   if (s.T == 0) return MOE_OK;
   Fp8Scales sc;
   r = fp8_args(s, experts, shared, &sc);
@@ -472,7 +472,7 @@ moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, const voi
   Shape s;
   moe_status r = to_shape(cfg, &s);
   if (r != MOE_OK) return r;
-  if (s.dtype != MOE_BF16 || !use_small_m(s)) return MOE_ERR_UNSUPPORTED;
+  if (s.dtype != MOE_BF16 || !small_m_fits(s)) return MOE_ERR_UNSUPPORTED;
   if (s.T == 0) return MOE_OK;
   Fp8Scales sc;
   r = fp8_args(s, experts, shared, &sc);

@@ -55,8 +55,15 @@ size_t permute_ws_bytes(const Shape& s);
 // Grouped MLP: tile table + intermediate activations.
 size_t grouped_ws_bytes(const Shape& s);
 
-// Small batches (every group has at most kSmallMMaxRows rows): weight-streaming kernels.
+// Small batches: the weight-streaming kernels run batches of at most kSmallMMaxRows tokens
+// (small_m_fits), the only path for FP8 expert weights. bf16 batches take them while the
+// experts average fewer than kSmallMRowsPerExpert rows (T*k < 8E, use_small_m); past that the
+// tiled GEMM reads the same weight bytes faster (measured on the Mixtral shape: 0.54 against
+// 0.55 ms at T = 32, 0.55 against 0.67 ms at T = 64; the weight-streaming path stays ahead
+// at 6 rows per expert and below).
 constexpr int kSmallMMaxRows = 64;
+constexpr int kSmallMRowsPerExpert = 8;
+bool small_m_fits(const Shape& s);
 bool use_small_m(const Shape& s);
 int small_m_splits(const Shape& s, bool gated);
 // K splits of the tiled down launch (1 or 2), from the widths only: a long K against a narrow
@@ -148,7 +155,7 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
 hipError_t launch_permute(const Shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_slot, int32_t* pos, uint8_t* drop, void* ws,
                           hipStream_t st);
-// fp8: scales of FP8 expert weights (the weight-streaming path only: the caller checks use_small_m)
+// fp8: scales of FP8 expert weights (the weight-streaming path only: the caller checks small_m_fits)
 hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sorted_slot,
                               const int32_t* offsets, const void* wg, const void* wu,
                               const void* wd, const void* swg, const void* swu, const void* swd,

@@ -1061,7 +1061,7 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
                               const void* wd, const void* swg, const void* swu, const void* swd,
                               void* y_perm, void* y_shared, void* ws, hipStream_t st, const Fp8Scales& fp8) {
   GroupedWs w = carve(s, ws);
-  if (use_small_m(s))
+  if (use_small_m(s) || (fp8.gate && small_m_fits(s)))
     return launch_grouped_mlp_small(s, x, sorted_slot, offsets, wg, wu, wd, swg, swu, swd, w.h, w.hs,
                                     w.part, y_perm, y_shared, st, fp8);
   if (fp8.gate) return hipErrorInvalidValue;  // FP8 weights: weight-streaming path only

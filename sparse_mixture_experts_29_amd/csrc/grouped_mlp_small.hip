@@ -449,7 +449,10 @@ int max_groups(const Shape& s) {
 
 }  // namespace
 
-bool use_small_m(const Shape& s) { return s.dtype == MOE_BF16 && s.T <= kSmallMMaxRows; }
+bool small_m_fits(const Shape& s) { return s.dtype == MOE_BF16 && s.T <= kSmallMMaxRows; }
+bool use_small_m(const Shape& s) {
+  return small_m_fits(s) && s.T * s.k < static_cast<int64_t>(kSmallMRowsPerExpert) * s.E;
+}
 
 hipError_t launch_split_reduce(const Shape& s, const float* part, int splits, const int32_t* offsets, void* y_perm,
                                void* y_shared, hipStream_t st) {
@@ -484,7 +487,7 @@ int small_m_splits(const Shape& s, bool gated) {
 }
 
 size_t small_m_ws_bytes(const Shape& s) {
-  if (!use_small_m(s)) return 0;
+  if (!small_m_fits(s)) return 0;  // also sized when bf16 batches take the tiled path (FP8 cannot)
   const int64_t rows_total = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
   const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
   const int sg = small_m_splits(s, true);

@@ -27,9 +27,13 @@ CASES = [
     R(configs.DEEPSEEK_V3, T=513, d_model=320, d_ff=128, n_experts=64, d_ff_shared=192),
     R(configs.DEEPSEEK_V3, T=200, d_model=256, d_ff=128, n_experts=300, top_k=8, n_shared=2,
       d_ff_shared=64),
+    # decode batches: T = 1, 4, 16 on the weight-streaming kernels, T = 64 (16 rows per
+    # expert) on the tiled GEMM
     *[R(configs.mixtral_decode(t), d_model=512, d_ff=1024) for t in (1, 4, 16, 64)],
     # small batches through the weight-streaming path, with a shared expert and a K tail
     R(configs.DEEPSEEK_V3, T=40, d_model=320, d_ff=192, n_experts=64, d_ff_shared=320),
+    R(configs.QWEN3_FINE_CF, T=57, d_model=256, d_ff=128, n_experts=64, top_k=4),
+    # the same with 16 experts: 14 rows per expert, so the tiled GEMM, capacity drops
     R(configs.QWEN3_FINE_CF, T=57, d_model=256, d_ff=128, n_experts=16, top_k=4),
     # tiled down launch with K split in two (d_ff >= 2 d_model), ragged tiles, with and
     # without a shared expert and capacity
@@ -140,10 +144,11 @@ def test_stream_argument_is_honoured():
 
 
 def test_small_batch_collapsed_router_fills_four_token_groups():
-    """64 tokens all routed to expert 5 first: one group of 64 rows (4 groups of 16)."""
-    cfg = R(configs.MIXTRAL_PREFILL, T=64, d_model=256, d_ff=512, n_experts=8, top_k=2)
+    """64 tokens all routed to expert 5 first: one group of 64 rows (4 groups of 16) on the
+    weight-streaming kernels (32 experts: 4 rows per expert on average)."""
+    cfg = R(configs.MIXTRAL_PREFILL, T=64, d_model=256, d_ff=512, n_experts=32, top_k=2)
     li = make_inputs(cfg)
-    li.router_bias = np.zeros(8, np.float32)
+    li.router_bias = np.zeros(32, np.float32)
     li.router_bias[5] = 4.0
     dev = DeviceLayer(li)
     P.check_layer_full(li, dev)
