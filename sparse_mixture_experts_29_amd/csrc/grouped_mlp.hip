@@ -454,74 +454,198 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
     }
   }
 
-  // epilogue. acc[i][j] register r of lane l: weight row (operand A) 8*(r/4) + 4*(l/32) + r%4
-  // of sub-tile i, token row 32*(2j + wm) + l%32.
-#pragma unroll
-  for (int j = 0; j < LIVE; ++j) {
-    const int row = row0 + (2 * j + wm) * 32 + l32;
-    if (row >= row1) continue;
-    // SAVE: the gate and up products themselves, side by side in a row of 2N; F32: fp32 sums
-    bf16_t* op = static_cast<bf16_t*>(out_v) + (out_row_base + row) * (SAVE ? 2 * N : N);
-    if (!GATED && F32) {
-      float* opf = static_cast<float*>(out_v) + (out_row_base + row) * N;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * 128 + i * 32 + q * 8 + khalf * 4;
-          if (n < N)
-            *reinterpret_cast<float4*>(opf + n) =
-                make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-        }
-    } else if (GATED && SAVE) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * 64 + i * 32 + q * 8 + khalf * 4;
-          if (n < N) {
-            uint2 pa, pb;
-            pa.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-            pa.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-            pb.x = pack_bf16x2(acc[i + 2][j][q * 4 + 0], acc[i + 2][j][q * 4 + 1]);
-            pb.y = pack_bf16x2(acc[i + 2][j][q * 4 + 2], acc[i + 2][j][q * 4 + 3]);
-            *reinterpret_cast<uint2*>(op + n) = pa;
-            *reinterpret_cast<uint2*>(op + N + n) = pb;
+  // epilogue. Gated outputs (64 h columns a wave) and fp32 split partials are stored straight
+  // from the accumulators; the bf16 products of the plain, save and weight-gradient modes go
+  // out through LDS (measured per tile: staging takes the plain epilogue from 15 k to 10 k
+  // cycles and the weight-gradient one from 21 k to 12 k, but costs the gated one 8% and the
+  // fp32 one 10% more).
+  constexpr bool STAGED = !F32 && (!GATED || SAVE);
+  if constexpr (!STAGED) {
+    // epilogue. acc[i][j] register r of lane l: weight row (operand A) 8*(r/4) + 4*(l/32) + r%4
+    // of sub-tile i, token row 32*(2j + wm) + l%32.
+  #pragma unroll
+    for (int j = 0; j < LIVE; ++j) {
+      const int row = row0 + (2 * j + wm) * 32 + l32;
+      if (row >= row1) continue;
+      // SAVE: the gate and up products themselves, side by side in a row of 2N; F32: fp32 sums
+      bf16_t* op = static_cast<bf16_t*>(out_v) + (out_row_base + row) * (SAVE ? 2 * N : N);
+      if (!GATED && F32) {
+        float* opf = static_cast<float*>(out_v) + (out_row_base + row) * N;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * 128 + i * 32 + q * 8 + khalf * 4;
+            if (n < N)
+              *reinterpret_cast<float4*>(opf + n) =
+                  make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
           }
-        }
-    } else if (GATED) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * 64 + i * 32 + q * 8 + khalf * 4;
-          if (n < N) {
-            float h[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float gv = acc[i][j][q * 4 + u];
-              const float uv = acc[i + 2][j][q * 4 + u];
-              h[u] = silu_f32(gv) * uv;
+      } else if (GATED && SAVE) {
+  #pragma unroll
+        for (int i = 0; i < 2; ++i)
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * 64 + i * 32 + q * 8 + khalf * 4;
+            if (n < N) {
+              uint2 pa, pb;
+              pa.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+              pa.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+              pb.x = pack_bf16x2(acc[i + 2][j][q * 4 + 0], acc[i + 2][j][q * 4 + 1]);
+              pb.y = pack_bf16x2(acc[i + 2][j][q * 4 + 2], acc[i + 2][j][q * 4 + 3]);
+              *reinterpret_cast<uint2*>(op + n) = pa;
+              *reinterpret_cast<uint2*>(op + N + n) = pb;
             }
-            uint2 pk;
-            pk.x = pack_bf16x2(h[0], h[1]);
-            pk.y = pack_bf16x2(h[2], h[3]);
-            *reinterpret_cast<uint2*>(op + n) = pk;
           }
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * 128 + i * 32 + q * 8 + khalf * 4;
-          if (n < N) {
-            uint2 pk;
-            pk.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-            pk.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-            *reinterpret_cast<uint2*>(op + n) = pk;
+      } else if (GATED) {
+  #pragma unroll
+        for (int i = 0; i < 2; ++i)
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * 64 + i * 32 + q * 8 + khalf * 4;
+            if (n < N) {
+              float h[4];
+  #pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const float gv = acc[i][j][q * 4 + u];
+                const float uv = acc[i + 2][j][q * 4 + u];
+                h[u] = silu_f32(gv) * uv;
+              }
+              uint2 pk;
+              pk.x = pack_bf16x2(h[0], h[1]);
+              pk.y = pack_bf16x2(h[2], h[3]);
+              *reinterpret_cast<uint2*>(op + n) = pk;
+            }
           }
+      } else {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * 128 + i * 32 + q * 8 + khalf * 4;
+            if (n < N) {
+              uint2 pk;
+              pk.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+              pk.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+              *reinterpret_cast<uint2*>(op + n) = pk;
+            }
+          }
+      }
+    }
+  } else {
+    // epilogue. acc[i][j] register r of lane l holds weight row (operand A) 8*(r/4) + 4*(l/32)
+    // + r%4 of sub-tile i and token row 32*(2j + wm) + l%32: a lane has 4 consecutive output
+    // columns of one token row, so a store straight from the registers touches 32 rows (32
+    // cache lines, 8 or 16 bytes each). Instead each wave stages its outputs in its own quarter
+    // of the stage ring, idle now, as token rows of its output columns (16-byte chunks
+    // XOR-swizzled by row), and reads back whole 16-byte chunks of a row per lane: a store
+    // instruction then writes 64 / CHR rows, each a contiguous CHR*16-byte segment.
+    // F32 (split partials, 512-byte rows) goes through in passes of SPP sub-tiles.
+    constexpr int CW = GATED && !SAVE ? 64 : 128;       // output columns of this wave
+    constexpr int ES = F32 ? 4 : 2;                     // bytes per output element
+    constexpr int CHR = CW * ES / 16;                   // 16-byte chunks per staged row: 8, 16, 32
+    constexpr int TJL = BT / 64;                        // token sub-tiles per wave
+    constexpr int SPP = F32 ? (BT == 256 ? 2 : 1) : TJL;  // token sub-tiles per pass
+    constexpr int QUARTER = BT == 256 ? 32768 : 16384;  // bytes of the ring per wave
+    static_assert(SPP * 32 * CHR * 16 <= QUARTER, "a pass fits the wave's quarter of the ring");
+    static_assert(4 * QUARTER <= NST * (BW + BT) * BK * 2, "the quarters fit the ring");
+    stage_barrier();  // every wave is done reading the last stage
+    char* stg = reinterpret_cast<char*>(lds) + wave * QUARTER;
+    // an opaque copy of the lane index: the staging addresses depend on the lane only, and
+    // the compiler would otherwise hoist all of them out of the persistent tile loop, keeping
+    // ~70 registers live through every K loop (and spilling)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int el32 = ln & 31, ekh = ln >> 5;
+    const int ld_out = SAVE ? 2 * N : N;
+  #pragma unroll
+    for (int p0 = 0; p0 < LIVE; p0 += SPP) {
+      // stage sub-tiles p0 .. p0+SPP-1 (those < LIVE): row lr = 32*(j - p0) + l%32
+  #pragma unroll
+      for (int j = p0; j < p0 + SPP && j < LIVE; ++j) {
+        const int lr = (j - p0) * 32 + el32;
+        char* srow = stg + lr * (CHR * 16);
+        auto put8 = [&](int chunk, uint2 v) {  // 8 bytes at half khalf of a 16-byte chunk
+          *reinterpret_cast<uint2*>(srow + ((chunk ^ (lr & (CHR - 1))) << 4) + ekh * 8) = v;
+        };
+        if constexpr (F32) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int chunk = i * 8 + q * 2 + ekh;  // columns i*32 + q*8 + khalf*4 .. +3
+              *reinterpret_cast<float4*>(srow + ((chunk ^ (lr & (CHR - 1))) << 4)) =
+                  make_float4(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+            }
+        } else if constexpr (GATED && SAVE) {
+  #pragma unroll
+          for (int i = 0; i < 2; ++i)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint2 pa, pb;
+              pa.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+              pa.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+              pb.x = pack_bf16x2(acc[i + 2][j][q * 4 + 0], acc[i + 2][j][q * 4 + 1]);
+              pb.y = pack_bf16x2(acc[i + 2][j][q * 4 + 2], acc[i + 2][j][q * 4 + 3]);
+              put8(i * 4 + q, pa);      // gate products: chunks 0..7
+              put8(8 + i * 4 + q, pb);  // up products: chunks 8..15
+            }
+        } else if constexpr (GATED) {
+  #pragma unroll
+          for (int i = 0; i < 2; ++i)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float h[4];
+  #pragma unroll
+              for (int u = 0; u < 4; ++u) h[u] = silu_f32(acc[i][j][q * 4 + u]) * acc[i + 2][j][q * 4 + u];
+              uint2 pk;
+              pk.x = pack_bf16x2(h[0], h[1]);
+              pk.y = pack_bf16x2(h[2], h[3]);
+              put8(i * 4 + q, pk);
+            }
+        } else {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint2 pk;
+              pk.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+              pk.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+              put8(i * 4 + q, pk);
+            }
         }
+      }
+      // read back: lane l takes chunk l % CHR of staged row it*(64/CHR) + l/CHR
+      constexpr int RPIT = 64 / CHR;  // staged rows per instruction
+      const int rows = (min(LIVE, p0 + SPP) - p0) * 32;
+  #pragma unroll
+      for (int it = 0; it < SPP * 32 / RPIT; ++it) {
+        const int lr = it * RPIT + ln / CHR;
+        if (it * RPIT >= rows) break;
+        const int c = ln % CHR;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + lr * (CHR * 16) + ((c ^ (lr & (CHR - 1))) << 4));
+        const int jt = p0 + lr / 32;  // this wave's sub-tile
+        const int row = row0 + (2 * jt + wm) * 32 + (lr & 31);
+        if (row >= row1) continue;
+        if constexpr (F32) {
+          const int n = n0 + wn * 128 + c * 4;
+          if (n < N)
+            *reinterpret_cast<uint4*>(static_cast<float*>(out_v) + (out_row_base + row) * N + n) = v;
+        } else {
+          bf16_t* op = static_cast<bf16_t*>(out_v) + (out_row_base + row) * ld_out;
+          int n, col;
+          if constexpr (GATED && SAVE) {
+            n = n0 + wn * 64 + (c & 7) * 8;
+            col = c < 8 ? n : N + n;
+          } else if constexpr (GATED) {
+            n = n0 + wn * 64 + c * 8;
+            col = n;
+          } else {
+            n = n0 + wn * 128 + c * 8;
+            col = n;
+          }
+          if (n < N) *reinterpret_cast<uint4*>(op + col) = v;
+        }
+      }
     }
   }
 }
