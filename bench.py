@@ -73,6 +73,31 @@ def kernel_source_hash(name: str) -> str:
     return source_hash(os.path.join(ROOT, "sparse_mixture_experts_29_amd", "csrc", name))
 
 
+def graph_steps(step, K: int, warmup: int, torch):
+    """One call of step() captured in a HIP graph (torch.cuda.CUDAGraph), then warmup + K
+    replays on the current stream, each timed with a pair of events. Returns per-replay ms."""
+    import numpy as np
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
 def traffic_from_profile(kernel_file: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
     on the current source of the kernel; otherwise None."""
@@ -389,6 +414,9 @@ def main():
                     help="also time K cold steps, each after writing this many MiB of scratch (the MALL "
                          "holds no weights at the step's start); reported under 'cold', not in value")
     ap.add_argument("--flush-mode", choices=("read", "write"), default="read")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time K replays of one layer step captured in a HIP graph (reported under "
+                         "'graph', never in value)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many MiB once (a plain copy "
                          "kernel of known size, to scale the HBM byte counters of a profiler run)")
@@ -528,6 +556,11 @@ def main():
             cold["gate_up_gbps"] = round(roofline["bytes_per_launch"] / (cold_gate.mean() * 1e-3) / 1e9, 1)
             cold["layer_hbm_frac"] = round(layer_bytes / (cold_ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
         out["cold"] = cold
+    if args.graph:
+        g_ms = graph_steps(dev.forward, K, args.warmup, torch)
+        out["graph"] = {"ms_per_step": round(float(g_ms.mean()), 4),
+                        "value": round(cfg.T / (g_ms.mean() * 1e-3), 1),
+                        "step_ms_p50": round(float(np.percentile(g_ms, 50)), 4)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(li, min(args.cpu_tokens, cfg.T))
     print(json.dumps(out), flush=True)

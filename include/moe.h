@@ -20,6 +20,9 @@
  *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work on it:
  *    they are asynchronous, never synchronise the host, and never copy data back.
  *    Calls on different streams with disjoint outputs and workspaces may overlap.
+ *    What a call enqueues is kernel launches only (no memset, copy or allocation), so a
+ *    call made while `stream` is being captured into a HIP graph replays as part of it,
+ *    reading its inputs at replay time.
  *  - Element type of x, every weight, y_perm, y_shared and y is cfg->dtype
  *    (MOE_F32: float; MOE_BF16: bfloat16 bit patterns). Accumulation is fp32.
  *    Router bias and gates are float; indices are int32.
