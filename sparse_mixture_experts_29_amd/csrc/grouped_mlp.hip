@@ -677,11 +677,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
     split = L / per;
     L -= split * per;
   }
-  const int in_group = kGroupM * n_n;
-  const int first_m = (L / in_group) * kGroupM;
-  const int gsz = min(n_m - first_m, kGroupM);
-  const int m_idx = first_m + (L % in_group) % gsz;
-  const int n_tile = (L % in_group) / gsz;
+  // raster groups: runs of m-tiles that sweep every n-tile together. A run of s m-tiles
+  // starting at m-tile f owns the tiles L in [f*n_n, (f+s)*n_n), so L / n_n is one of its
+  // m-tiles, whose table entry names the run (entry 3: f | s << 24). Runs are chunks of one
+  // group's m-tiles (weight-gradient launches: kGroupM m-tiles in order)
+  int first_m, gsz;
+  if constexpr (WGRAD) {
+    first_m = (L / (kGroupM * n_n)) * kGroupM;
+    gsz = min(n_m - first_m, kGroupM);
+  } else {
+    const int run = __builtin_amdgcn_readfirstlane(a.tiles[(L / n_n) * kTileEntries + 3]);
+    first_m = run & 0xFFFFFF;
+    gsz = run >> 24;
+  }
+  const int local = L - first_m * n_n;
+  const int m_idx = first_m + local % gsz;
+  const int n_tile = local / gsz;
 
   // tile bookkeeping is wave-uniform: keep it in scalar registers
   int g, row0, row1;
@@ -990,6 +1001,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgsF32 a) {
 }
 
 // ------------------------------------------------------------------- tile table
+// Raster run of m-tile i of a group whose n m-tiles start at m-tile `first`: the group's
+// m-tiles in ceil(n / kGroupM) runs of near-equal size (9 -> 5 + 4), so that the tiles an XCD
+// runs at once share one group's weight tiles. Encoded as run start | run size << 24.
+__device__ __forceinline__ int32_t raster_run(int first, int n, int i) {
+  const int nc = (n + kGroupM - 1) / kGroupM;
+  const int base = n / nc, rem = n % nc;  // rem runs of base + 1, then runs of base
+  int start, size;
+  if (i < rem * (base + 1)) {
+    start = (i / (base + 1)) * (base + 1);
+    size = base + 1;
+  } else {
+    start = rem * (base + 1) + ((i - rem * (base + 1)) / base) * base;
+    size = base;
+  }
+  return (first + start) | (size << 24);
+}
+
 // One block: per-group tile counts, exclusive scan, then the entries.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int E, int n_shared, int T, int bm,
@@ -1019,7 +1047,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     t[0] = e;
     t[1] = base_row + i * bm;
     t[2] = min(base_row + (i + 1) * bm, base_row + rows);
-    t[3] = 0;
+    t[3] = raster_run(first, mine, i);
   }
   const int routed_tiles = scan[1023];
   const int per_shared = (T + bm - 1) / bm;
@@ -1029,7 +1057,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     t[0] = E + s;
     t[1] = m * bm;
     t[2] = min((m + 1) * bm, T);
-    t[3] = 0;
+    t[3] = raster_run(routed_tiles + s * per_shared, per_shared, m);
   }
   if (e == 0) *n_tiles = routed_tiles + n_shared * per_shared;
 }
