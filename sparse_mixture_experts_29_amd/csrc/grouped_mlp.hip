@@ -650,6 +650,23 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
   }
 }
 
+// Raster run of m-tile i of a group whose n m-tiles start at m-tile `first`: the group's
+// m-tiles in ceil(n / kGroupM) runs of near-equal size (9 -> 5 + 4), so that the tiles an XCD
+// runs at once share one group's weight tiles. Encoded as run start | run size << 24.
+__device__ __forceinline__ int32_t raster_run(int first, int n, int i) {
+  const int nc = (n + kGroupM - 1) / kGroupM;
+  const int base = n / nc, rem = n % nc;  // rem runs of base + 1, then runs of base
+  int start, size;
+  if (i < rem * (base + 1)) {
+    start = (i / (base + 1)) * (base + 1);
+    size = base + 1;
+  } else {
+    start = rem * (base + 1) + ((i - rem * (base + 1)) / base) * base;
+    size = base;
+  }
+  return (first + start) | (size << 24);
+}
+
 // One tile: BW weight rows x BT token rows, 4 waves as 2 (weights) x 2 (tokens), each
 // wave 128 weight rows x BT/2 tokens (alternate 32-row sub-tiles) of
 // v_mfma_f32_32x32x16_bf16 accumulators. L is the
@@ -679,17 +696,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
   }
   // raster groups: runs of m-tiles that sweep every n-tile together. A run of s m-tiles
   // starting at m-tile f owns the tiles L in [f*n_n, (f+s)*n_n), so L / n_n is one of its
-  // m-tiles, whose table entry names the run (entry 3: f | s << 24). Runs are chunks of one
-  // group's m-tiles (weight-gradient launches: kGroupM m-tiles in order)
-  int first_m, gsz;
+  // m-tiles, which names the run: entry 3 of its tile-table entry (f | s << 24), or, for the
+  // weight-gradient launches (a fixed mt_r / mt_s m-tiles per group), the same chunking
+  // computed in place
+  int run;
+  const int q = L / n_n;
   if constexpr (WGRAD) {
-    first_m = (L / (kGroupM * n_n)) * kGroupM;
-    gsz = min(n_m - first_m, kGroupM);
+    const int routed_m = a.E * a.mt_r;
+    if (q < routed_m) {
+      const int i = q % a.mt_r;
+      run = raster_run(q - i, a.mt_r, i);
+    } else {
+      const int i = (q - routed_m) % a.mt_s;
+      run = raster_run(q - i, a.mt_s, i);
+    }
   } else {
-    const int run = __builtin_amdgcn_readfirstlane(a.tiles[(L / n_n) * kTileEntries + 3]);
-    first_m = run & 0xFFFFFF;
-    gsz = run >> 24;
+    run = a.tiles[q * kTileEntries + 3];
   }
+  run = __builtin_amdgcn_readfirstlane(run);
+  const int first_m = run & 0xFFFFFF;
+  const int gsz = run >> 24;
   const int local = L - first_m * n_n;
   const int m_idx = first_m + local % gsz;
   const int n_tile = local / gsz;
@@ -1001,23 +1027,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgsF32 a) {
 }
 
 // ------------------------------------------------------------------- tile table
-// Raster run of m-tile i of a group whose n m-tiles start at m-tile `first`: the group's
-// m-tiles in ceil(n / kGroupM) runs of near-equal size (9 -> 5 + 4), so that the tiles an XCD
-// runs at once share one group's weight tiles. Encoded as run start | run size << 24.
-__device__ __forceinline__ int32_t raster_run(int first, int n, int i) {
-  const int nc = (n + kGroupM - 1) / kGroupM;
-  const int base = n / nc, rem = n % nc;  // rem runs of base + 1, then runs of base
-  int start, size;
-  if (i < rem * (base + 1)) {
-    start = (i / (base + 1)) * (base + 1);
-    size = base + 1;
-  } else {
-    start = rem * (base + 1) + ((i - rem * (base + 1)) / base) * base;
-    size = base;
-  }
-  return (first + start) | (size << 24);
-}
-
 // One block: per-group tile counts, exclusive scan, then the entries.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int E, int n_shared, int T, int bm,
