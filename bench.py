@@ -411,8 +411,9 @@ def main():
                     help="time the training step (forward + moe_layer_backward) of the workload")
     ap.add_argument("--aux-coef", type=float, default=0.01, help="balancing-loss coefficient (--backward)")
     ap.add_argument("--flush-mib", type=int, default=0,
-                    help="also time K cold steps, each after writing this many MiB of scratch (the MALL "
-                         "holds no weights at the step's start); reported under 'cold', not in value")
+                    help="also time K cold steps, each after streaming this many MiB of scratch through "
+                         "the caches (read, or written with --flush-mode write), so the MALL holds no "
+                         "weights at the step's start; reported under 'cold', not in value")
     ap.add_argument("--flush-mode", choices=("read", "write"), default="read")
     ap.add_argument("--graph", action="store_true",
                     help="also time K replays of one layer step captured in a HIP graph (reported under "
