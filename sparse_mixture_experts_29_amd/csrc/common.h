@@ -52,6 +52,9 @@ constexpr int kPermuteChunk = 1024;  // (token, slot) pairs per chunk (one wave 
 int64_t permute_chunks(const Shape& s);
 size_t permute_ws_bytes(const Shape& s);
 
+// compute units of the current device (cached per device; 256 if the query fails)
+int cu_count();
+
 // Grouped MLP: tile table + intermediate activations.
 size_t grouped_ws_bytes(const Shape& s);
 

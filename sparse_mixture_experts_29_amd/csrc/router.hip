@@ -18,10 +18,10 @@ namespace moe {
 namespace {
 
 constexpr int kRouterThreads = 256;
-#ifndef MOE_ROUTER_BT
-#define MOE_ROUTER_BT 32
-#endif
-constexpr int kRouterBT = MOE_ROUTER_BT;  // tokens per block of the bf16 MFMA router
+// tokens per block of the bf16 MFMA router: 32, or 64 for batches that still give every CU a
+// block (every block reads all of W_r, so 64-token blocks halve those reads)
+constexpr int kRouterBT = 32;
+constexpr int kRouterBTLarge = 64;
 
 // One step of a wave argmax (key: larger logit, then lower index) against the lane that
 // the DPP pattern CTRL selects within each row of 16 lanes.
@@ -502,10 +502,15 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
   timing_begin(MOE_KERNEL_ROUTER, st);
   if (s.dtype == MOE_BF16) {
     // 32 tokens per block: twice the blocks of a 64-token tile, two waves per SIMD, and the
-    // logits tile of even E = 1024 fits LDS (32 x 1028 x 4 B)
-    constexpr int BT = kRouterBT;
+    // logits tile of even E = 1024 fits LDS (32 x 1028 x 4 B). 64 tokens once T gives every
+    // CU a 64-token block and E <= 256 (a 66.5 KB logits tile): every block reads all of W_r,
+    // and at that size those reads are the router's time (DeepSeek-shaped, T = 16384,
+    // E = 256, d = 7168: 335 -> 236 us); below it the idle CUs cost more (qwen3_fine, T = 8192:
+    // 48 -> 79 us).
+    const bool large = s.E <= 256 && T / kRouterBTLarge >= cu_count();
+    const int BT = large ? kRouterBTLarge : kRouterBT;
     const size_t lds = static_cast<size_t>(BT) * (s.E + 4) * sizeof(float);
-    auto kern = router_bf16_kernel<BT>;
+    auto kern = large ? router_bf16_kernel<kRouterBTLarge> : router_bf16_kernel<kRouterBT>;
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(lds));
     hipLaunchKernelGGL(kern, dim3((T + BT - 1) / BT), block, lds, st, static_cast<const bf16_t*>(x),

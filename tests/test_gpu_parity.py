@@ -143,6 +143,19 @@ def test_stream_argument_is_honoured():
     assert torch.equal(dev.y, ref)
 
 
+def test_route_of_a_batch_large_enough_for_64_token_router_blocks():
+    """T = 16384 with E = 256: the router takes 64-token blocks (T / 64 >= the CU count);
+    expert sets, order, gates and logits against the oracle."""
+    cfg = R(configs.DEEPSEEK_V3, T=16384, d_model=256, d_ff=64, n_experts=256, top_k=8, n_shared=0)
+    P.say(f"case {cfg.name}")
+    li = make_inputs(cfg)
+    dev = DeviceLayer(li)
+    b = dev.stage_buffers()
+    dev.route(b)
+    torch.cuda.synchronize()
+    P.check_route(li, dev, b)
+
+
 def test_small_batch_collapsed_router_fills_four_token_groups():
     """64 tokens all routed to expert 5 first: one group of 64 rows (4 groups of 16) on the
     weight-streaming kernels (32 experts: 4 rows per expert on average)."""
