@@ -370,9 +370,8 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   LayerWs w = layer_layout(s, ws);
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_route(s, x, w_router, router_bias, w.idx, w.gate, nullptr, st);
-  if (e == hipSuccess)
-    e = launch_permute(s, w.idx, w.counts, w.offsets, w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
+  hipError_t e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
+                                      w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
   if (use_small_m(s)) {
     // small batches: combine straight from the down launch's split-K partials (no y_perm
     // round trip, one launch fewer; the same values as the staged calls)
@@ -484,9 +483,8 @@ moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, const voi
   const moe_fp8_weights* sh = s.n_shared > 0 ? shared : nullptr;
   // the small-batch sequence of moe_layer_forward: the combine reads the down launch's
   // split-K partials
-  hipError_t e = launch_route(s, x, w_router, router_bias, w.idx, w.gate, nullptr, st);
-  if (e == hipSuccess)
-    e = launch_permute(s, w.idx, w.counts, w.offsets, w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
+  hipError_t e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
+                                      w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
   if (e == hipSuccess)
     e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, experts->w_gate, experts->w_up, experts->w_down,
                            sh ? sh->w_gate : nullptr, sh ? sh->w_up : nullptr, sh ? sh->w_down : nullptr, nullptr,
@@ -519,9 +517,9 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
   const int T = static_cast<int>(s.T);
   hipError_t e = launch_fill_u32(w.ctrl, 64, 0, st);
   // forward state: routing, permutation, tile table
-  if (e == hipSuccess) e = launch_route(s, x, w_router, router_bias, w.idx, w.gate, w.logits, st);
   if (e == hipSuccess)
-    e = launch_permute(s, w.idx, w.counts, w.offsets, w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
+    e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, w.logits, w.counts, w.offsets,
+                             w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
   if (e == hipSuccess) e = launch_build_tiles(s, w.offsets, w.tiles, w.ctrl, w.ctrl + 16, st);
   GemmLaunch L{};
   L.tiles = w.tiles;

@@ -158,6 +158,12 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
 hipError_t launch_permute(const Shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_slot, int32_t* pos, uint8_t* drop, void* ws,
                           hipStream_t st);
+// launch_route then launch_permute, as one launch when both fit one block (small batches);
+// the same results either way
+hipError_t launch_route_permute(const Shape& s, const void* x, const void* w_router, const float* bias,
+                                int32_t* idx, float* gate, float* logits, int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_slot, int32_t* pos, uint8_t* drop, void* permute_ws,
+                                hipStream_t st);
 // fp8: scales of FP8 expert weights (the weight-streaming path only: the caller checks small_m_fits)
 hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sorted_slot,
                               const int32_t* offsets, const void* wg, const void* wu,

@@ -12,7 +12,7 @@
 // The bf16 K loop reads 32 contiguous bytes per lane per operand per 64-wide K block and
 // feeds them to 2 MFMAs; the MFMA sees a permuted K order, identical for both operands, so
 // the dot products are unchanged.
-#include "common.h"
+#include "permute_block.h"
 
 namespace moe {
 namespace {
@@ -375,15 +375,15 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
 // thread folds one value over 32 lanes, then each logit over the 8 groups of lanes; wave w
 // then runs top-k and the gates for token w.
 template <typename T, int EMAX, int TB>
-__global__ __launch_bounds__(256) void router_small_e_kernel(
+__device__ __forceinline__ void router_small_e_block(
     const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
     int32_t* __restrict__ idx, float* __restrict__ gate, float* __restrict__ logits, int n_tok,
-    int d, int E, int k, int gating) {
+    int d, int E, int k, int gating, int blk) {
   static_assert(TB * EMAX == 32, "32 partial sums per lane");
   __shared__ float part[256][33];  // +1: rows fall on distinct banks
   __shared__ float red[8][32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * TB;
+  const int t0 = blk * TB;
   float acc[TB * EMAX];
 #pragma unroll
   for (int i = 0; i < TB * EMAX; ++i) acc[i] = 0.f;
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256) void router_small_e_kernel(
   }
   __syncthreads();
   const int t = t0 + wave;
-  if (wave >= TB || t >= n_tok) return;
+  if (wave >= TB || t >= n_tok) return;  // (the caller's block continues past this function)
   float my = -INFINITY;
   if (lane < E) {
     const int j = wave * EMAX + lane;
@@ -475,6 +475,33 @@ __global__ __launch_bounds__(256) void router_small_e_kernel(
   }
 }
 
+
+template <typename T, int EMAX, int TB>
+__global__ __launch_bounds__(256) void router_small_e_kernel(
+    const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
+    int32_t* __restrict__ idx, float* __restrict__ gate, float* __restrict__ logits, int n_tok,
+    int d, int E, int k, int gating) {
+  router_small_e_block<T, EMAX, TB>(x, w, bias, idx, gate, logits, n_tok, d, E, k, gating, blockIdx.x);
+}
+
+// Route and permute in one launch when both fit one block (the router's single block of TB
+// tokens, at most kPermuteChunk pairs): the block's top-k writes reach global memory, the
+// barrier makes them visible to the whole block, and the block then runs the one-block
+// permute on them. Saves a launch and its gap on decode steps; the results are those of the
+// two separate launches.
+template <typename T, int EMAX, int TB>
+__global__ __launch_bounds__(256) void route_permute_single_kernel(
+    const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
+    int32_t* __restrict__ idx, float* __restrict__ gate, float* __restrict__ logits, int n_tok,
+    int d, int E, int k, int gating, int ebits, int64_t capacity, int64_t max_kept,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ pos, uint8_t* __restrict__ drop) {
+  __shared__ int plds[permute_block_lds_ints(EMAX)];
+  router_small_e_block<T, EMAX, TB>(x, w, bias, idx, gate, logits, n_tok, d, E, k, gating, 0);
+  __syncthreads();
+  permute_single_block(idx, static_cast<int64_t>(n_tok) * k, E, ebits, capacity, max_kept, counts, offsets,
+                       sorted_slot, pos, drop, plds);
+}
 }  // namespace
 
 hipError_t launch_route(const Shape& s, const void* x, const void* w_router, const float* bias,
@@ -526,6 +553,38 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
     hipLaunchKernelGGL(kern, dim3((T + BT - 1) / BT), block, lds, st, static_cast<const float*>(x),
                        static_cast<const float*>(w_router), bias, idx, gate, logits, T, s.d, s.E,
                        s.k, s.gating);
+  }
+  timing_end(MOE_KERNEL_ROUTER, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const Shape& s, const void* x, const void* w_router, const float* bias,
+                                int32_t* idx, float* gate, float* logits, int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_slot, int32_t* pos, uint8_t* drop, void* permute_ws,
+                                hipStream_t st) {
+  const int T = static_cast<int>(s.T);
+  // one router block (E <= 8: 4 tokens; E <= 32: 1 token) and one permute chunk
+  const bool e8 = s.E <= 8;
+  const bool one_block = (e8 && T <= 4) || (s.E <= 32 && T == 1);
+  if (!one_block || s.T * s.k > kPermuteChunk) {
+    hipError_t e = launch_route(s, x, w_router, bias, idx, gate, logits, st);
+    if (e == hipSuccess) e = launch_permute(s, idx, counts, offsets, sorted_slot, pos, drop, permute_ws, st);
+    return e;
+  }
+  int ebits = 0;
+  while ((1 << ebits) < s.E) ++ebits;
+  timing_begin(MOE_KERNEL_ROUTER, st);
+  const dim3 g(1), b(kRouterThreads);
+  if (s.dtype == MOE_BF16) {
+    auto kern = e8 ? route_permute_single_kernel<bf16_t, 8, 4> : route_permute_single_kernel<bf16_t, 32, 1>;
+    hipLaunchKernelGGL(kern, g, b, 0, st, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_router), bias,
+                       idx, gate, logits, T, s.d, s.E, s.k, s.gating, ebits, s.capacity, s.max_kept, counts, offsets,
+                       sorted_slot, pos, drop);
+  } else {
+    auto kern = e8 ? route_permute_single_kernel<float, 8, 4> : route_permute_single_kernel<float, 32, 1>;
+    hipLaunchKernelGGL(kern, g, b, 0, st, static_cast<const float*>(x), static_cast<const float*>(w_router), bias,
+                       idx, gate, logits, T, s.d, s.E, s.k, s.gating, ebits, s.capacity, s.max_kept, counts, offsets,
+                       sorted_slot, pos, drop);
   }
   timing_end(MOE_KERNEL_ROUTER, st);
   return hipGetLastError();
