@@ -147,6 +147,50 @@ def time_steps(step, K: int, warmup: int, stream, kernel=None):
     return elapsed, step_ms, gate_up_ms
 
 
+def blas_name(info) -> str:
+    """The BLAS library numpy runs the oracle's products on (threadpoolctl's report)."""
+    libs = [f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in info if i.get("user_api") == "blas"]
+    return ", ".join(libs) or "unknown"
+
+
+def sample_clocks(step, want: int = 2, seconds: float = 8.0) -> dict:
+    """rocm-smi's current clocks, read (want times, at most `seconds`) while step() runs in a
+    loop on the GPU after the timed steps; the clocks are not controlled. On any failure the
+    reason is returned instead of samples."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+    tool = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    samples, errors = [], []
+
+    def poll():
+        t_end = time.time() + seconds
+        while time.time() < t_end and len(samples) < want:
+            try:
+                r = subprocess.run([tool, "--showclocks", "--json"], capture_output=True, text=True,
+                                   timeout=seconds)
+                card = next(iter(json.loads(r.stdout).values()))
+                samples.append({k.split(" clock")[0]: str(v).strip("()") for k, v in card.items()
+                                if "clock speed" in k})
+            except Exception as e:  # the tool is missing, refused or printed something else
+                errors.append(f"{type(e).__name__}: {e}"[:200])
+                return
+
+    th = threading.Thread(target=poll)
+    th.start()
+    while th.is_alive():
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    out = {"tool": "rocm-smi --showclocks --json", "while": "layer steps after the timed ones", "samples": samples}
+    if errors:
+        out["error"] = errors[0]
+    return out
+
+
 def cold_steps(step, K: int, stream, flush_mib: int, mode: str = "read"):
     """K steps, each after streaming a flush_mib MiB scratch buffer through the caches so that
     the MALL holds none of the weights; each step timed alone with events around it (the flush
@@ -361,7 +405,7 @@ def cpu_baseline_backward(li, n_tokens: int, aux: float):
     oracle.backward(x, wr, li.router_bias, dy, top_k=c.top_k, gating=c.gating, capacity_factor=c.capacity_factor,
                     experts=experts, shared=shared, n_shared=c.n_shared, aux_coef=aux)
     dt = time.perf_counter() - t0
-    return dict(value=n_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+    return dict(value=n_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle", blas=blas_name(info),
                 sample=f"forward + backward of the first {n_tokens} of {c.T} tokens of {c.name} "
                        f"(capacity and balancing loss over that sample); {dt:.1f} s", seconds=round(dt, 2))
 
@@ -392,7 +436,7 @@ def cpu_baseline(li, n_tokens: int):
                    n_shared=c.n_shared)
     dt = time.perf_counter() - t0
     del experts
-    return dict(value=n_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+    return dict(value=n_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle", blas=blas_name(info),
                 sample=f"first {n_tokens} of {c.T} tokens of {c.name}, the chosen experts' "
                        f"weights {'decoded from FP8' if c.fp8 else 'widened'} to float64 inside the timed "
                        f"region; {dt:.1f} s",
@@ -470,7 +514,12 @@ def main():
     elapsed, step_ms, gate_up_ms = time_steps(dev.forward, args.steps, args.warmup, stream)
     K = args.steps
     value = cfg.T * K / elapsed
+    # after the timed steps: the down launch in a pass of its own, then the clocks while the
+    # layer runs
+    _, _, down_ms = time_steps(dev.forward, K, 1, stream, kernel=binding.MOE_KERNEL_DOWN)
+    clocks = sample_clocks(dev.forward)
     flops_gate_up = 4.0 * cfg.d_model * cfg.d_ff * n_kept + 4.0 * cfg.d_model * cfg.d_ff_shared * cfg.T * cfg.n_shared
+    flops_down = flops_gate_up / 2
     layer_flops = (cfg.expert_flops_per_pair() * n_kept + cfg.shared_flops() + cfg.router_flops())
     es = 2 if cfg.dtype == "bf16" else 4
     small_batch = cfg.dtype == "bf16" and cfg.T <= SMALL_BATCH_TOKENS
@@ -541,11 +590,20 @@ def main():
             "layer_tflops": round(layer_flops / (np.median(step_ms) * 1e-3) / 1e12, 2),
             "layer_mfma_frac": round(layer_flops / (np.median(step_ms) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "layer_hbm_frac": round(layer_bytes / (np.median(step_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "pairs_per_s": round(n_kept / (np.median(step_ms) * 1e-3), 1),
+            "gate_up_avg_ms": round(float(gate_up_ms.mean()), 4),
+            "down_avg_ms": round(float(down_ms.mean()), 4),
             "n_kept": n_kept,
             "experts_touched": touched,
             "max_over_mean_load": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
         },
+        "clocks": clocks,
     }
+    if cfg.dtype == "bf16" and not small_batch:
+        # both grouped launches (gate/up, down; shared experts ride in them as extra groups)
+        gemm_tflops = (flops_gate_up + flops_down) / ((gate_up_ms.mean() + down_ms.mean()) * 1e-3) / 1e12
+        out["layer"]["grouped_gemm_tflops"] = round(gemm_tflops, 2)
+        out["layer"]["grouped_gemm_mfma_frac"] = round(gemm_tflops / BF16_PEAK_TFLOPS, 4)
     if args.flush_mib:
         cold_ms, cold_gate = cold_steps(dev.forward, K, stream, args.flush_mib, args.flush_mode)
         cold = {"flush_mib": args.flush_mib, "flush_mode": args.flush_mode,
