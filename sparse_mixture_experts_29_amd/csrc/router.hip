@@ -60,15 +60,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& e) {
   e = be;
 }
 
-// Row (16-lane) versions of the argmax and of a sum: after the four DPP steps every lane of
-// a row holds the row's result.
-__device__ __forceinline__ void row_argmax(float& v, int& e) {
-  dpp_argmax_step<0xB1>(v, e);   // lane ^ 1
-  dpp_argmax_step<0x4E>(v, e);   // lane ^ 2
-  dpp_argmax_step<0x141>(v, e);  // half-row mirror
-  dpp_argmax_step<0x140>(v, e);  // row mirror
-}
-
+// Row (16-lane) sum: after the four DPP steps every lane of a row holds the row's sum.
 template <int CTRL>
 __device__ __forceinline__ float dpp_sum_step(float v) {
   return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -81,47 +73,78 @@ __device__ __forceinline__ float row_sum(float v) {
   return dpp_sum_step<0x140>(v);
 }
 
-// Top-k and gates for E <= 256: each row of 16 lanes owns one token (a wave runs 4 tokens at
-// once) and lane li holds the candidates li, li+16, ... in registers; k rounds of row_argmax
-// pick the experts in descending order. Slot j is kept by lane j % 16 (k <= 32).
-template <int BT>
+// Selection key of expert e with logit v: one unsigned 64-bit compare orders candidates by
+// larger logit, then lower index (the selection rule). High word: the logit's bits mapped so
+// that unsigned order is float order (-0 taken as +0, so the zeros tie; NaN below -inf, so it
+// is chosen last); low word: 0x7FFFFFFF - e. Keys are distinct for distinct experts.
+__device__ __forceinline__ uint64_t select_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
+  uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  o = (u & 0x7FFFFFFFu) > 0x7F800000u ? 0u : o;
+  return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(0x7FFFFFFF - e);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return 0x7FFFFFFF - static_cast<int>(static_cast<uint32_t>(key)); }
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t o = static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_max_key_step(uint64_t& v) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, 0xF, 0xF, false));
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  v = o > v ? o : v;
+}
+
+// Row (16-lane) maximum of a key: lane ^ 1, lane ^ 2 (quad permutes), then the half-row and
+// row mirrors, which pair every lane with one across the halves already reduced; afterwards
+// every lane of the row holds the row's maximum.
+__device__ __forceinline__ uint64_t row_max_key(uint64_t v) {
+  dpp_max_key_step<0xB1>(v);
+  dpp_max_key_step<0x4E>(v);
+  dpp_max_key_step<0x141>(v);
+  dpp_max_key_step<0x140>(v);
+  return v;
+}
+
+// Top-k and gates for E <= 16 R: each row of 16 lanes owns one token (a wave runs 4 tokens at
+// once) and lane li holds the selection keys of candidates li, li+16, ... in registers. Round
+// j takes the row maximum among keys below the previous winner's (keys are distinct, so this
+// walks the candidates in selection order). Slot j is kept by lane j % 16 (k <= 32).
+template <int BT, int R>
 __device__ void topk_rows(const float* lg, int ld, int t0, int T, int E, int k, int gating, int32_t* idx,
                           float* gate) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, rq = lane >> 4;
   constexpr int kTokPerWave = BT / 4;
-  constexpr int RMAX = 16;      // E <= 256
-  const int R = (E + 15) / 16;  // candidates per lane
   for (int tt = 0; tt < kTokPerWave; tt += 4) {
     const int tl = wave * kTokPerWave + tt + rq;
     const int t = t0 + tl;
     const bool live = tt + rq < kTokPerWave && t < T;
     const float* row = lg + (live ? tl : 0) * ld;
-    float cand[RMAX];
+    uint64_t key[R];
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
+    for (int r = 0; r < R; ++r) {
       const int e = li + 16 * r;
-      cand[r] = (r < R && e < E) ? row[e] : -INFINITY;
+      key[r] = e < E ? select_key(row[e], e) : 0ull;  // 0: below every real key
     }
-    uint32_t taken = 0;  // bit r: candidate li + 16 r already chosen
+    uint64_t last = ~0ull;
     float first = 0.f, my_l[2] = {0.f, 0.f};
     int my_e[2] = {0, 0};
     for (int j = 0; j < k; ++j) {
-      float bl = -INFINITY;
-      int be = 0x7fffffff;
+      uint64_t best = 0;
 #pragma unroll
-      for (int r = 0; r < RMAX; ++r) {
-        const int e = li + 16 * r;
-        const bool ok = r < R && e < E && !((taken >> r) & 1u);
-        const bool better = cand[r] > bl || (cand[r] == bl && e < be);
-        bl = ok && better ? cand[r] : bl;
-        be = ok && better ? e : be;
-      }
-      row_argmax(bl, be);
-      if ((be & 15) == li) taken |= 1u << (be >> 4);
+      for (int r = 0; r < R; ++r) best = key[r] < last && key[r] > best ? key[r] : best;
+      best = row_max_key(best);
+      last = best;
+      const float bl = key_logit(best);
       if (li == (j & 15)) {
         my_l[j >> 4] = bl;
-        my_e[j >> 4] = be;
+        my_e[j >> 4] = key_expert(best);
       }
       if (j == 0) first = bl;
     }
@@ -199,6 +222,21 @@ __device__ void topk_and_gates(const float* lg, int ld, int t0, int T, int E, in
       gate[static_cast<int64_t>(t) * k + lane] = p / sum;
     }
   }
+}
+
+// Top-k and gates from a block's logits in LDS: E <= 256 by rows of 16 lanes with as few
+// candidates per lane as E needs, larger E by whole waves.
+template <int BT>
+__device__ __forceinline__ void topk_block(const float* lg, int ld, int t0, int T, int E, int k, int gating, int32_t* idx,
+                           float* gate) {
+  if (E <= 64)
+    topk_rows<BT, 4>(lg, ld, t0, T, E, k, gating, idx, gate);
+  else if (E <= 128)
+    topk_rows<BT, 8>(lg, ld, t0, T, E, k, gating, idx, gate);
+  else if (E <= 256)
+    topk_rows<BT, 16>(lg, ld, t0, T, E, k, gating, idx, gate);
+  else
+    topk_and_gates<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
 }
 
 // One pass of the bf16 router for one wave: NJ expert tiles of 16 (tiles p0 + wave + 4j) x
@@ -324,10 +362,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(
       if (t0 + tl < T) logits[static_cast<int64_t>(t0 + tl) * E + e] = lg[tl * ld + e];
     }
   }
-  if (E <= 256)
-    topk_rows<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
-  else
-    topk_and_gates<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
+  topk_block<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
 }
 
 template <int BT>
@@ -361,10 +396,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
       if (t0 + tl < T) logits[static_cast<int64_t>(t0 + tl) * E + e] = lg[tl * ld + e];
     }
   }
-  if (E <= 256)
-    topk_rows<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
-  else
-    topk_and_gates<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
+  topk_block<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
 }
 
 // Small expert counts (E <= 32): a block of 256 threads owns TB tokens and splits d over all
