@@ -7,8 +7,10 @@
 // Larger E: one block of 256 threads owns BT tokens and every expert:
 //   1. logits tile [BT][E] accumulated in fp32 (bf16: MFMA 16x16x32, W_r rows as the A
 //      operand, token rows as B; fp32: plain FMA) and parked in LDS;
-//   2. each wave takes BT/4 tokens and runs k rounds of a wave-wide argmax over the
-//      token's E logits (key: larger logit, then lower index), then the gates.
+//   2. each wave takes BT/4 tokens (E <= 256: a row of 16 lanes per token) and runs k
+//      rounds of a maximum over the token's selection keys, one 64-bit key per expert that
+//      orders by larger logit, then lower index; then the gates.
+// Every path (also the small-E kernel) selects through the same keys.
 // The bf16 K loop reads 32 contiguous bytes per lane per operand per 64-wide K block and
 // feeds them to 2 MFMAs; the MFMA sees a permuted K order, identical for both operands, so
 // the dot products are unchanged.
@@ -22,43 +24,6 @@ constexpr int kRouterThreads = 256;
 // block (every block reads all of W_r, so 64-token blocks halve those reads)
 constexpr int kRouterBT = 32;
 constexpr int kRouterBTLarge = 64;
-
-// One step of a wave argmax (key: larger logit, then lower index) against the lane that
-// the DPP pattern CTRL selects within each row of 16 lanes.
-template <int CTRL>
-__device__ __forceinline__ void dpp_argmax_step(float& v, int& e) {
-  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-  const int oe = __builtin_amdgcn_update_dpp(0, e, CTRL, 0xF, 0xF, false);
-  if (ov > v || (ov == v && oe < e)) {
-    v = ov;
-    e = oe;
-  }
-}
-
-// Wave argmax of (v, e), returned in every lane (wave-uniform). Within each row of 16 lanes:
-// DPP swaps with lane^1 and lane^2 (quad permutes), then the half-row and row mirrors, which
-// pair every lane with one across the halves already reduced; the four row winners (lanes
-// 0, 16, 32, 48) are then compared in scalar registers. DPP moves cost a VALU cycle, a
-// cross-lane shuffle through the LDS unit about a hundred.
-__device__ __forceinline__ void wave_argmax(float& v, int& e) {
-  dpp_argmax_step<0xB1>(v, e);   // quad_perm [1,0,3,2]: lane ^ 1
-  dpp_argmax_step<0x4E>(v, e);   // quad_perm [2,3,0,1]: lane ^ 2
-  dpp_argmax_step<0x141>(v, e);  // row_half_mirror: lane i <-> 7 - i in each 8
-  dpp_argmax_step<0x140>(v, e);  // row_mirror: lane i <-> 15 - i in each 16
-  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  int be = __builtin_amdgcn_readlane(e, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
-    const int oe = __builtin_amdgcn_readlane(e, 16 * r);
-    if (ov > bv || (ov == bv && oe < be)) {
-      bv = ov;
-      be = oe;
-    }
-  }
-  v = bv;
-  e = be;
-}
 
 // Row (16-lane) sum: after the four DPP steps every lane of a row holds the row's sum.
 template <int CTRL>
@@ -109,6 +74,26 @@ __device__ __forceinline__ uint64_t row_max_key(uint64_t v) {
   dpp_max_key_step<0x141>(v);
   dpp_max_key_step<0x140>(v);
   return v;
+}
+
+__device__ __forceinline__ uint64_t read_key_lane(uint64_t v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Wave maximum of a key, returned wave-uniform: the row maxima, then the four row winners
+// (lanes 0, 16, 32, 48) compared after readlane. DPP moves cost a VALU cycle; a cross-lane
+// shuffle through the LDS unit about a hundred.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = row_max_key(v);
+  uint64_t b = read_key_lane(v, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const uint64_t o = read_key_lane(v, 16 * r);
+    b = o > b ? o : b;
+  }
+  return b;
 }
 
 // Top-k and gates for E <= 16 R: each row of 16 lanes owns one token (a wave runs 4 tokens at
@@ -169,8 +154,9 @@ __device__ void topk_rows(const float* lg, int ld, int t0, int T, int E, int k, 
 }
 
 // Top-k and gates of the tokens of a block, from their logits in LDS (row tl at lg + tl*ld).
-// Each wave takes BT/4 tokens; lane l holds the candidates l, l+64, ... (E <= 1024) in
-// registers and k rounds of wave_argmax pick the experts in descending order.
+// Each wave takes BT/4 tokens; lane l holds the selection keys of candidates l, l+64, ...
+// (E <= 1024) and k rounds of a wave maximum over the keys below the previous winner's pick
+// the experts in descending order.
 template <int BT>
 __device__ void topk_and_gates(const float* lg, int ld, int t0, int T, int E, int k, int gating,
                                int32_t* idx, float* gate) {
@@ -183,32 +169,25 @@ __device__ void topk_and_gates(const float* lg, int ld, int t0, int T, int E, in
     const int t = t0 + tl;
     if (t >= T) break;
     const float* row = lg + tl * ld;
-    float cand[RMAX];
+    uint64_t key[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       const int e = lane + 64 * r;
-      cand[r] = (r < R && e < E) ? row[e] : -INFINITY;
+      key[r] = (r < R && e < E) ? select_key(row[e], e) : 0ull;
     }
-    uint32_t taken = 0;  // bit r: candidate lane + 64 r already chosen
+    uint64_t last = ~0ull;
     float first = 0.f, my_l = 0.f;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
-      // lane-local best among untaken candidates
-      float bl = -INFINITY;
-      int be = 0x7fffffff;
+      uint64_t best = 0;
 #pragma unroll
-      for (int r = 0; r < RMAX; ++r) {
-        const int e = lane + 64 * r;
-        if (r < R && e < E && !((taken >> r) & 1u) && (cand[r] > bl || (cand[r] == bl && e < be))) {
-          bl = cand[r];
-          be = e;
-        }
-      }
-      wave_argmax(bl, be);
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
+      for (int r = 0; r < RMAX; ++r) best = key[r] < last && key[r] > best ? key[r] : best;
+      best = wave_max_key(best);
+      last = best;
+      const float bl = key_logit(best);
       if (lane == j) {
         my_l = bl;
-        my_e = be;
+        my_e = key_expert(best);
       }
       if (j == 0) first = bl;
     }
@@ -227,8 +206,8 @@ __device__ void topk_and_gates(const float* lg, int ld, int t0, int T, int E, in
 // Top-k and gates from a block's logits in LDS: E <= 256 by rows of 16 lanes with as few
 // candidates per lane as E needs, larger E by whole waves.
 template <int BT>
-__device__ __forceinline__ void topk_block(const float* lg, int ld, int t0, int T, int E, int k, int gating, int32_t* idx,
-                           float* gate) {
+__device__ __forceinline__ void topk_block(const float* lg, int ld, int t0, int T, int E, int k, int gating,
+                                           int32_t* idx, float* gate) {
   if (E <= 64)
     topk_rows<BT, 4>(lg, ld, t0, T, E, k, gating, idx, gate);
   else if (E <= 128)
@@ -485,16 +464,16 @@ __device__ __forceinline__ void router_small_e_block(
     my = sum + (bias ? bias[lane] : 0.f);
   }
   if (logits && lane < E) logits[static_cast<int64_t>(t) * E + lane] = my;
-  // top-k: k rounds of a wave argmax (larger logit, then lower index)
-  bool taken = false;
+  // top-k: k rounds of a wave maximum over the selection keys below the previous winner's
+  const uint64_t key = lane < E ? select_key(my, lane) : 0ull;
+  uint64_t last = ~0ull;
   float first = 0.f, mine_l = 0.f;
   int mine_e = 0;
   for (int j = 0; j < k; ++j) {
-    float bl = (lane < E && !taken) ? my : -INFINITY;
-    int be = (lane < E && !taken) ? lane : 0x7fffffff;
-    wave_argmax(bl, be);
-    if (lane == be) taken = true;
-    if (lane == j) { mine_l = bl; mine_e = be; }
+    const uint64_t best = wave_max_key(key < last ? key : 0ull);
+    last = best;
+    const float bl = key_logit(best);
+    if (lane == j) { mine_l = bl; mine_e = key_expert(best); }
     if (j == 0) first = bl;
   }
   float p = 0.f;

@@ -12,6 +12,7 @@ import torch
 from sparse_mixture_experts_29_amd import configs
 from sparse_mixture_experts_29_amd.device import DeviceLayer
 from sparse_mixture_experts_29_amd.inputs import make_inputs
+import oracle
 from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
@@ -154,6 +155,58 @@ def test_route_of_a_batch_large_enough_for_64_token_router_blocks():
     dev.route(b)
     torch.cuda.synchronize()
     P.check_route(li, dev, b)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (1024, 32)], ids=["small_e", "rows", "wave"])
+def test_nan_logits_are_chosen_last_and_the_zeros_tie(E, k):
+    """Each router path (E = 8: vector-ALU kernel; 128: MFMA logits, top-k on 16-lane rows;
+    1024: top-k over whole waves) against the selection rule on non-finite and signed-zero
+    logits, as the oracle's stable sort applies it (NaN sorts after every number). A token with
+    a NaN activation has NaN logits everywhere: no larger logit decides, so it takes experts
+    0..k-1 with NaN gates. A NaN bias makes that expert's logit NaN for every token: it is
+    never chosen while k < E. On zero router weights the logits tie (zeros of either sign), so
+    after the one expert with a positive bias the lower indices win. The other tokens route
+    exactly as without the NaN."""
+    P.say(f"case E={E} k={k}")
+    cfg = R(configs.QWEN3_FINE, T=70, d_model=128, d_ff=64, n_experts=E, top_k=k, router_bias="none")
+    li = make_inputs(cfg)
+    dev = DeviceLayer(li)
+    b = dev.stage_buffers()
+    dev.route(b)
+    torch.cuda.synchronize()
+    idx0, gate0 = P.host(b["idx"]).copy(), P.host(b["gate"]).copy()
+
+    nan_bf16 = torch.tensor([float("nan")], dtype=torch.bfloat16, device=dev.device)
+    dev.x[5, 3] = nan_bf16[0]
+    dev.route(b)
+    torch.cuda.synchronize()
+    idx, gate = P.host(b["idx"]), P.host(b["gate"])
+    assert (idx[5] == np.arange(k)).all() and np.isnan(gate[5]).all()
+    assert (oracle.select_topk(np.full((1, E), np.nan), k)[0] == np.arange(k)).all()
+    rest = np.arange(cfg.T) != 5
+    assert (idx[rest] == idx0[rest]).all() and np.array_equal(gate[rest], gate0[rest])
+
+    bias = np.zeros(E, np.float32)
+    bias[2] = np.nan
+    dev.router_bias = torch.from_numpy(bias).to(dev.device)
+    dev.route(b)
+    torch.cuda.synchronize()
+    assert not (P.host(b["idx"])[rest] == 2).any()
+    one_nan = np.zeros((1, E))
+    one_nan[0, 2] = np.nan
+    assert 2 not in oracle.select_topk(one_nan, k)[0]
+
+    dev.w_router.zero_()
+    bias = np.zeros(E, np.float32)
+    bias[1] = -0.0
+    bias[4] = 1.0
+    dev.router_bias = torch.from_numpy(bias).to(dev.device)
+    dev.route(b)
+    torch.cuda.synchronize()
+    idx = P.host(b["idx"])
+    want = np.array([4] + [e for e in range(E) if e != 4][: k - 1])
+    assert (idx[rest] == want).all()
+    assert (oracle.select_topk(bias[None, :].astype(np.float64), k)[0] == want).all()
 
 
 def test_small_batch_collapsed_router_fills_four_token_groups():
