@@ -344,6 +344,167 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(
   topk_block<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
 }
 
+// ---------------------------------------------------------------- LDS-staged logits (bf16)
+// E <= 256: the logits tile [BT][E] of a block from operands staged through LDS by
+// direct-to-LDS loads. A direct operand load of the 16x16x32 MFMA touches 16 rows, 16 cache
+// lines, per instruction, and a loop built on such loads ran at the rate of its load
+// instructions (dropping either operand's loads halved it); a DMA instruction fills 8 whole
+// 128-byte rows (1 KB). A stage holds EW rows of W_r (E rounded up to a multiple of 64; rows
+// past E repeat row E-1 and their logits are dropped), then the BT token rows (past T: row
+// T-1), 64 k (128 bytes) per row; 16-byte chunk slot p of row r holds the row's chunk
+// p ^ (r & 7), so the 16 rows of an operand read spread over the banks. The ring holds as
+// many stages as fit about 120 KB (3..8): with little MFMA work per stage, its bytes in
+// flight are what hide the load latency.
+__host__ __device__ constexpr int router_lds_rows(int BT, int EW) { return EW + BT; }
+__host__ __device__ constexpr int router_lds_nst(int BT, int EW) {
+  return 122880 / (router_lds_rows(BT, EW) * 128) > 8   ? 8
+         : 122880 / (router_lds_rows(BT, EW) * 128) < 3 ? 3
+                                                         : 122880 / (router_lds_rows(BT, EW) * 128);
+}
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maximum (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void router_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// this wave's DMA of the current stage has landed once at most `later` later stages (IPW
+// instructions each) are still in flight
+template <int IPW, int NST>
+__device__ __forceinline__ void router_wait_stage(int later) {
+  static_assert(NST <= 8 && (NST - 2) * IPW < 64, "the wait counter holds the stages in flight");
+  switch (later) {
+    case 0: router_wait_vmcnt<0>(); break;
+    case 1: router_wait_vmcnt<IPW>(); break;
+    case 2: router_wait_vmcnt<(NST > 3 ? 2 : 1) * IPW>(); break;
+    case 3: router_wait_vmcnt<(NST > 4 ? 3 : 1) * IPW>(); break;
+    case 4: router_wait_vmcnt<(NST > 5 ? 4 : 1) * IPW>(); break;
+    case 5: router_wait_vmcnt<(NST > 6 ? 5 : 1) * IPW>(); break;
+    default: router_wait_vmcnt<(NST > 7 ? 6 : 1) * IPW>(); break;
+  }
+}
+
+// bare workgroup barrier: every wave has already waited for its own DMA (__syncthreads
+// would also drain the DMA still in flight); the empty asm keeps memory accesses in place
+__device__ __forceinline__ void router_stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct-to-LDS 16-byte load: lane l's 16 bytes at g land at LDS byte address m0 + 16 l. No
+// register result; M0 is written here and declared clobbered, one wait state before use.
+// The loop orders it with its own vmcnt waits and barriers.
+__device__ __forceinline__ void router_dma16(const char* g, uint32_t lds_byte) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m0v) : "memory", "m0");
+}
+
+typedef __attribute__((address_space(3))) void router_lds_void;
+
+template <int BT, int EW>
+__global__ __launch_bounds__(kRouterThreads) void router_bf16_lds_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const float* __restrict__ bias,
+    int32_t* __restrict__ idx, float* __restrict__ gate, float* __restrict__ logits, int T, int d,
+    int E, int k, int gating) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];  // the stage ring, then the logits
+  constexpr int ROWS = router_lds_rows(BT, EW);
+  constexpr int STAGE = ROWS * 128;  // bytes
+  constexpr int IPW = ROWS / 32;     // DMA instructions per wave per stage (8 rows each)
+  constexpr int NST = router_lds_nst(BT, EW);
+  constexpr int NJ = EW / 64;  // expert tiles of 16 per wave (tiles wave, wave + 4, ...)
+  constexpr int NT = BT / 16;  // token tiles of 16
+  static_assert(ROWS % 32 == 0 && EW % 64 == 0, "whole DMA instructions per wave");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int quad = lane >> 4, l16 = lane & 15;
+  const int t0 = blockIdx.x * BT;
+  const int nkb = d / 64;
+
+  // instruction i of this wave fills stage rows 8 q .. 8 q + 7, q = 4 i + wave; lane l takes
+  // row 8 q + l / 8 and stores its chunk slot l % 8 = logical chunk (l % 8) ^ (row & 7)
+  const char* src[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int r = 8 * (4 * i + wave) + (lane >> 3);
+    const int p = (lane & 7) ^ (r & 7);
+    const bf16_t* row = r < EW ? w + static_cast<int64_t>(min(r, E - 1)) * d
+                               : x + static_cast<int64_t>(min(t0 + r - EW, T - 1)) * d;
+    src[i] = reinterpret_cast<const char*>(row) + p * 16;
+  }
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((router_lds_void*)smem));
+  auto issue = [&](int kb) {
+    const uint32_t st = lds0 + static_cast<uint32_t>((kb % NST) * STAGE);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) router_dma16(src[i] + static_cast<int64_t>(kb) * 128, st + (4 * i + wave) * 1024);
+  };
+  // operand byte offsets within a stage, k half c: row r, logical chunk 4 c + quad
+  int aoff[NJ][2], boff[NT][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = 16 * (wave + 4 * j) + l16;
+      aoff[j][c] = r * 128 + (((4 * c + quad) ^ (r & 7)) * 16);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = EW + 16 * nt + l16;
+      boff[nt][c] = r * 128 + (((4 * c + quad) ^ (r & 7)) * 16);
+    }
+  }
+
+  f32x4 acc[NJ][NT];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[j][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nkb) issue(s);
+  for (int kb = 0; kb < nkb; ++kb) {
+    router_wait_stage<IPW, NST>(min(NST - 2, nkb - 1 - kb));
+    router_stage_barrier();  // stage kb is complete; every wave is done with stage kb - 1's slot
+    if (kb + NST - 1 < nkb) issue(kb + NST - 1);
+    const char* st = smem + (kb % NST) * STAGE;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 a[NJ], b[NT];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) a[j] = *reinterpret_cast<const u32x4*>(st + aoff[j][c]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) b[nt] = *reinterpret_cast<const u32x4*>(st + boff[nt][c]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[j][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[j]),
+                                                               __builtin_bit_cast(bf16x8, b[nt]), acc[j][nt], 0, 0, 0);
+    }
+  }
+  router_stage_barrier();  // every wave is done reading the ring; the logits tile reuses it
+  float* lg = reinterpret_cast<float*>(smem);
+  const int ld = E + 4;
+  // C layout (16x16): lane holds rows (experts) 4 quad + r of its tile, column (token) l16
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 16 * (wave + 4 * j) + quad * 4 + r;
+        if (e < E) lg[(nt * 16 + l16) * ld + e] = acc[j][nt][r] + (bias ? bias[e] : 0.f);
+      }
+  __syncthreads();
+  if (logits) {
+    for (int i = threadIdx.x; i < BT * E; i += kRouterThreads) {
+      const int tl = i / E, e = i - tl * E;
+      if (t0 + tl < T) logits[static_cast<int64_t>(t0 + tl) * E + e] = lg[tl * ld + e];
+    }
+  }
+  topk_block<BT>(lg, ld, t0, T, E, k, gating, idx, gate);
+}
+
 template <int BT>
 __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
@@ -547,13 +708,31 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
     // 48 -> 79 us).
     const bool large = s.E <= 256 && T / kRouterBTLarge >= cu_count();
     const int BT = large ? kRouterBTLarge : kRouterBT;
-    const size_t lds = static_cast<size_t>(BT) * (s.E + 4) * sizeof(float);
-    auto kern = large ? router_bf16_kernel<kRouterBTLarge> : router_bf16_kernel<kRouterBT>;
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(lds));
-    hipLaunchKernelGGL(kern, dim3((T + BT - 1) / BT), block, lds, st, static_cast<const bf16_t*>(x),
-                       static_cast<const bf16_t*>(w_router), bias, idx, gate, logits, T, s.d, s.E,
-                       s.k, s.gating);
+    const size_t lg_bytes = static_cast<size_t>(BT) * (s.E + 4) * sizeof(float);
+    if (s.E <= 256) {
+      // operands through LDS; the ring (then the logits tile) is one dynamic LDS array
+      const int EW = s.E <= 64 ? 64 : (s.E <= 128 ? 128 : 256);
+      const size_t ring = static_cast<size_t>(router_lds_nst(BT, EW)) * router_lds_rows(BT, EW) * 128;
+      const size_t lds = std::max(ring, lg_bytes);
+      auto kern = large ? (EW == 64 ? router_bf16_lds_kernel<kRouterBTLarge, 64>
+                                    : EW == 128 ? router_bf16_lds_kernel<kRouterBTLarge, 128>
+                                                : router_bf16_lds_kernel<kRouterBTLarge, 256>)
+                        : (EW == 64 ? router_bf16_lds_kernel<kRouterBT, 64>
+                                    : EW == 128 ? router_bf16_lds_kernel<kRouterBT, 128>
+                                                : router_bf16_lds_kernel<kRouterBT, 256>);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(lds));
+      hipLaunchKernelGGL(kern, dim3((T + BT - 1) / BT), block, lds, st, static_cast<const bf16_t*>(x),
+                         static_cast<const bf16_t*>(w_router), bias, idx, gate, logits, T, s.d, s.E,
+                         s.k, s.gating);
+    } else {
+      auto kern = router_bf16_kernel<kRouterBT>;
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(lg_bytes));
+      hipLaunchKernelGGL(kern, dim3((T + kRouterBT - 1) / kRouterBT), block, lg_bytes, st,
+                         static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_router), bias, idx, gate,
+                         logits, T, s.d, s.E, s.k, s.gating);
+    }
   } else {
     const bool small_e = s.E <= 256;
     const int BT = small_e ? 64 : 16;
