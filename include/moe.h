@@ -124,7 +124,9 @@ MOE_API moe_status moe_workspace_size(const moe_config* cfg, int op, size_t* byt
 
 /* Router (pages: "The router"; Q&A "How does a top-k router work?").
  *   logits[t][e] = sum_i x[t][i] * w_router[e][i] + router_bias[e]   (fp32 accumulate)
- *   topk_idx[t][j], j < k: the k largest logits, descending, ties to the lower index;
+ *   topk_idx[t][j], j < k: the k largest logits, descending, ties to the lower index
+ *   (-0 and +0 tie; a NaN logit ranks below every number, so a token whose logits are all
+ *   NaN takes experts 0..k-1 and NaN gates: every index is a valid expert);
  *   topk_gate[t][j]: softmax over the chosen logits (= softmax over all E renormalised
  *   over the chosen k), or sigmoid(l) / sum of the chosen sigmoid(l) for MOE_SIGMOID.
  * router_bias [E] float may be NULL (no bias). logits [T][E] float may be NULL. */
