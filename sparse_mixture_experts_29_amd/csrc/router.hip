@@ -700,12 +700,11 @@ hipError_t launch_route(const Shape& s, const void* x, const void* w_router, con
   const dim3 block(kRouterThreads);
   timing_begin(MOE_KERNEL_ROUTER, st);
   if (s.dtype == MOE_BF16) {
-    // 32 tokens per block: twice the blocks of a 64-token tile, two waves per SIMD, and the
-    // logits tile of even E = 1024 fits LDS (32 x 1028 x 4 B). 64 tokens once T gives every
-    // CU a 64-token block and E <= 256 (a 66.5 KB logits tile): every block reads all of W_r,
-    // and at that size those reads are the router's time (DeepSeek-shaped, T = 16384,
-    // E = 256, d = 7168: 335 -> 236 us); below it the idle CUs cost more (qwen3_fine, T = 8192:
-    // 48 -> 79 us).
+    // 32 tokens per block, or 64 once T gives every CU a 64-token block and E <= 256: every
+    // block reads all of W_r, so larger blocks read it fewer times, while below that T the
+    // idle CUs cost more (measured on the direct-load kernel: DeepSeek-shaped, T = 16384,
+    // E = 256, d = 7168: 335 -> 236 us with 64; qwen3_fine, T = 8192: 48 -> 79 us). The
+    // logits tile of E = 1024 still fits LDS at 32 tokens (32 x 1028 x 4 B).
     const bool large = s.E <= 256 && T / kRouterBTLarge >= cu_count();
     const int BT = large ? kRouterBTLarge : kRouterBT;
     const size_t lg_bytes = static_cast<size_t>(BT) * (s.E + 4) * sizeof(float);
