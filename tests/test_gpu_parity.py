@@ -157,6 +157,34 @@ def test_route_of_a_batch_large_enough_for_64_token_router_blocks():
     P.check_route(li, dev, b)
 
 
+LDS_ROUTER = [
+    # E not a multiple of 16 (part of the last 64-row block of W_r past E), one K block, ragged T
+    R(configs.QWEN3_FINE, T=300, d_model=64, d_ff=64, n_experts=33, top_k=3),
+    # sigmoid with a bias, E = 48, a two-block batch with a short last block
+    R(configs.DEEPSEEK_V3, T=70, d_model=128, d_ff=64, n_experts=48, top_k=4, n_shared=0),
+    # 128-row W_r blocks, three K blocks, 6 of 100
+    R(configs.QWEN3_FINE, T=129, d_model=192, d_ff=64, n_experts=100, top_k=6),
+    # 256-row W_r blocks (the three-stage ring), five K blocks
+    R(configs.DEEPSEEK_V3, T=1000, d_model=320, d_ff=64, n_experts=200, top_k=8, n_shared=0),
+    # 64-token blocks with a ragged last block of 5 tokens
+    R(configs.DEEPSEEK_V3, T=16389, d_model=128, d_ff=64, n_experts=256, top_k=8, n_shared=0),
+]
+
+
+@pytest.mark.parametrize("cfg", LDS_ROUTER, ids=lambda c: c.name)
+def test_router_with_operands_staged_through_lds(cfg):
+    """The bf16 router for 32 < E <= 256 stages W_r and the token rows through LDS (E rounded
+    up to a multiple of 64 rows, 64 k per stage, a ring of 3 to 8 stages): expert sets,
+    order, gates and logits against the oracle across the shapes that change its layout."""
+    P.say(f"case {cfg.name}")
+    li = make_inputs(cfg)
+    dev = DeviceLayer(li)
+    b = dev.stage_buffers()
+    dev.route(b)
+    torch.cuda.synchronize()
+    P.check_route(li, dev, b)
+
+
 @pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (1024, 32)], ids=["small_e", "rows", "wave"])
 def test_nan_logits_are_chosen_last_and_the_zeros_tie(E, k):
     """Each router path (E = 8: vector-ALU kernel; 128: MFMA logits, top-k on 16-lane rows;
