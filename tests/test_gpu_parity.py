@@ -75,6 +75,12 @@ EDGE = [
     R(configs.QWEN3_FINE, T=1, d_model=128, d_ff=64, n_experts=128, top_k=8),
     # many experts with no tokens
     R(configs.QWEN3_FINE, T=3, d_model=128, d_ff=128, n_experts=1024, top_k=32),
+    # route and permute in one launch: E <= 32 at T = 1 (sigmoid, shared expert; capacity 1)
+    R(configs.DEEPSEEK_V3, T=1, d_model=256, d_ff=128, n_experts=32, top_k=4, d_ff_shared=128),
+    R(configs.QWEN3_FINE_CF, T=1, d_model=128, d_ff=64, n_experts=16, top_k=2),
+    # ... and E <= 8 with a partly filled 4-token block, bf16 and fp32
+    R(configs.MIXTRAL_PREFILL, T=3, d_model=256, d_ff=128, n_experts=8, top_k=2),
+    R(configs.TINY_FP32, T=2),
 ]
 
 
