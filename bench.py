@@ -4,12 +4,16 @@
 
 A step is one moe_layer_forward (route, permute, grouped gate/up + SiLU*mul GEMM,
 grouped down GEMM, combine) over the workload's seeded synthetic batch, all inputs
-resident in HBM. The default workload is the Mixtral-shaped prefill layer (T=4096,
-d=4096, f=14336, E=8, top-2, bf16). Prints ONE JSON line (rank 0):
+resident in HBM. The default workload is the largest single-GPU layer, the DeepSeek-V3-style
+one (T=16384, d=7168, f=2048, E=256 routed experts, top-8, sigmoid gates, one shared expert,
+22.6 GB of bf16 weights). Prints ONE JSON line (rank 0):
   value      routed tokens per second (T * K / elapsed over the K timed steps)
   roofline   the gated grouped GEMM (the dominant kernel): algorithmic FLOPs per launch
-             (4 d f N_kept) / its average launch time, HIP events recorded around that
-             launch on the layer's stream inside the timed steps, against 2.5 PFLOP/s
+             (4 d f N_kept, + 4 d f_s T for the shared experts) / its average launch time,
+             HIP events recorded around that launch on the layer's stream inside the timed
+             steps, against 2.5 PFLOP/s
+  routing    expert loads, drops and near-tie tokens of the batch (outside the timed steps)
+  parity     the run's output against the oracle on the CPU baseline's tokens
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 Decode workloads (T <= 64) are bound by the touched experts' weight bytes (the weight-streaming
 kernels; bf16 batches averaging 8 or more rows per expert take the tiled GEMM): there the
@@ -175,9 +179,15 @@ def sample_clocks(step, want: int = 2, seconds: float = 8.0) -> dict:
             try:
                 r = subprocess.run([tool, "--showclocks", "--json"], capture_output=True, text=True,
                                    timeout=seconds)
-                card = next(iter(json.loads(r.stdout).values()))
-                samples.append({k.split(" clock")[0]: str(v).strip("()") for k, v in card.items()
-                                if "clock speed" in k})
+                got = {}
+                for card in json.loads(r.stdout).values():  # every card-like entry
+                    if isinstance(card, dict):
+                        got.update({k.split(" clock")[0].strip(): str(v).strip("()") for k, v in card.items()
+                                    if "clk" in k.lower() or "clock" in k.lower()})
+                if not got:
+                    errors.append("no clock fields in: " + r.stdout[:200])
+                    return
+                samples.append(got)
             except Exception as e:  # the tool is missing, refused or printed something else
                 errors.append(f"{type(e).__name__}: {e}"[:200])
                 return
@@ -415,7 +425,8 @@ def cpu_baseline_backward(li, n_tokens: int, aux: float):
 
 
 def cpu_baseline(li, n_tokens: int):
-    """The oracle (as it stands) on the first n_tokens of the workload, on host cores."""
+    """The oracle (as it stands) on the first n_tokens of the workload, on host cores.
+    Returns the record and the oracle's result on those tokens (its routing and y)."""
     import numpy as np
     import threadpoolctl
 
@@ -430,25 +441,122 @@ def cpu_baseline(li, n_tokens: int):
         experts = lambda e: oracle.fp8_expert(*codes[e])  # noqa: E731
         shared = lambda s: oracle.fp8_expert(*scodes[s])  # noqa: E731
     else:
-        experts = [li.expert_values(e) for e in range(c.n_experts)]  # input generation: untimed
-        shared = [li.shared_values(s) for s in range(c.n_shared)]
+        # stored weights (bf16 bit patterns, 2 bytes each) drawn untimed; the chosen experts'
+        # values are widened inside the timed region
+        store = [None] * c.n_experts
+
+        def put(e, w):
+            store[e] = w
+
+        li.for_each_expert(put, 16)
+        sstore = [li.shared(s) for s in range(c.n_shared)]
+        experts = lambda e: tuple(li.values(w) for w in store[e])  # noqa: E731
+        shared = lambda s: tuple(li.values(w) for w in sstore[s])  # noqa: E731
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     # the median of 3 runs when one run is short (the small and decode batches), else one run
     times = []
+    res = None
     while len(times) < (3 if not times or times[0] < CPU_REPEAT_BELOW_S else 1):
         t0 = time.perf_counter()
-        oracle.forward(x, wr, li.router_bias, top_k=c.top_k, gating=c.gating,
-                       capacity_factor=c.capacity_factor, experts=experts, shared=shared,
-                       n_shared=c.n_shared)
+        res = oracle.forward(x, wr, li.router_bias, top_k=c.top_k, gating=c.gating,
+                             capacity_factor=c.capacity_factor, experts=experts, shared=shared,
+                             n_shared=c.n_shared)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
-    del experts
-    return dict(value=n_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle", blas=blas_name(info),
-                sample=f"first {n_tokens} of {c.T} tokens of {c.name}, the chosen experts' "
-                       f"weights {'decoded from FP8' if c.fp8 else 'widened'} to float64 inside the timed "
-                       f"region; median of {len(times)} run(s), {dt:.3g} s each",
-                runs=len(times), seconds=round(dt, 2))
+    rec = dict(value=n_tokens / dt, unit="tokens/s", cores=int(threads), kind="oracle", blas=blas_name(info),
+               sample=f"first {n_tokens} of {c.T} tokens of {c.name}, the chosen experts' "
+                      f"weights {'decoded from FP8' if c.fp8 else 'widened'} to float64 inside the timed "
+                      f"region; median of {len(times)} run(s), {dt:.3g} s each",
+               runs=len(times), seconds=round(dt, 2))
+    return rec, res, (experts, shared)
+
+
+def routing_telemetry(li, counts, drop, idx_g, n_kept):
+    """Expert loads and drops of the timed batch (the library's own counts), and its near-tie
+    tokens: the oracle's float64 logits of every token, the k-th/(k+1)-th gap and adjacent
+    chosen logits closer than 1e-4, and how many tokens the GPU routed to another expert set
+    or in another order. Outside the timed steps."""
+    import numpy as np
+
+    import oracle
+    c = li.cfg
+    logits = oracle.router_logits(li.values(li.x), li.values(li.w_router), li.router_bias)
+    idx_o = oracle.select_topk(logits, c.top_k)
+    srt_o = -np.sort(-logits, axis=1)
+    gap = srt_o[:, c.top_k - 1] - srt_o[:, c.top_k] if c.top_k < c.n_experts else np.full(c.T, np.inf)
+    sel = np.take_along_axis(logits, idx_o, axis=1)
+    adj = ((sel[:, :-1] - sel[:, 1:]) < 1e-4).any(axis=1) if c.top_k > 1 else np.zeros(c.T, bool)
+    same_set = (np.sort(idx_g, axis=1) == np.sort(idx_o, axis=1)).all(axis=1)
+    pairs = c.T * c.top_k
+    cap = oracle.expert_capacity(c.capacity_factor, c.T, c.top_k, c.n_experts)
+    kept = counts if cap is None else np.minimum(counts, cap)
+    nz = counts[counts > 0]
+    return {
+        "pairs": pairs, "n_kept": n_kept, "capacity": cap,
+        "dropped": int(drop.sum()), "drop_rate": round(float(drop.sum()) / pairs, 6),
+        "experts_touched": int((counts > 0).sum()),
+        "load": {"max": int(counts.max()), "min": int(counts.min()), "min_nonzero": int(nz.min()) if nz.size else 0,
+                 "mean": round(float(counts.mean()), 2), "p50": float(np.percentile(counts, 50)),
+                 "p99": float(np.percentile(counts, 99)), "max_over_mean": round(float(counts.max() / counts.mean()), 3),
+                 "cv": round(float(counts.std() / counts.mean()), 4), "experts_over_capacity":
+                 None if cap is None else int((counts > cap).sum()),
+                 "kept_max_over_mean": round(float(kept.max() / max(kept.mean(), 1e-9)), 3)},
+        "near_tie_tokens": int((gap < 1e-4).sum()),
+        "adjacent_near_tie_tokens": int((adj & (gap >= 1e-4)).sum()),
+        "tokens_routed_to_another_set": int((~same_set).sum()),
+        "order_flips": int(((idx_g != idx_o).any(axis=1) & same_set).sum()),
+        "near_tie_rule": "float64 oracle logits: k-th/(k+1)-th gap < 1e-4, or adjacent chosen logits < 1e-4 apart",
+    }, (logits, idx_o)
+
+
+def parity_against_oracle(li, y_dev, idx_g, drop_g, base_res, weights, oracle_routing):
+    """The run's y on the CPU baseline's tokens against the oracle (its own routing). Tokens
+    the GPU routed to another expert set, or whose kept experts differ, are near ties: counted
+    and left out. Dropless layers reuse the baseline's y; with a capacity the oracle's token
+    outputs are recomputed with the drops of the whole batch."""
+    import numpy as np
+
+    import oracle
+    c = li.cfg
+    n = base_res["y"].shape[0]
+    if c.dropless:
+        idx_o, y_o = base_res["idx"], base_res["y"]
+        keep_o = np.ones_like(idx_o, dtype=bool)
+    else:
+        logits, idx_all = oracle_routing
+        gate_all = oracle.gate_values(logits, idx_all, c.gating)
+        cap = oracle.expert_capacity(c.capacity_factor, c.T, c.top_k, c.n_experts)
+        keep_all = oracle.permute(idx_all, c.n_experts, cap)["drop"].reshape(c.T, c.top_k) == 0
+        idx_o, keep_o = idx_all[:n], keep_all[:n]
+        y_o = oracle.token_outputs(li.values(li.x[:n]), idx_o, gate_all[:n], keep_o, weights[0], weights[1],
+                                   c.n_shared)
+    keep_g = drop_g.reshape(c.T, c.top_k)[:n] == 0
+    ig = idx_g[:n]
+    same = (np.sort(ig, axis=1) == np.sort(idx_o, axis=1)).all(axis=1)
+    kept_same = np.array([sorted(ig[t][keep_g[t]]) == sorted(idx_o[t][keep_o[t]]) for t in range(n)])
+    ok = same & kept_same
+    got = y_dev[:n].float().cpu().numpy().astype(np.float64)[ok]
+    want = np.asarray(y_o, np.float64)[ok]
+    diff = got - want
+    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(want), 1e-30))
+    mx = float(np.abs(diff).max(initial=0))
+    bf16 = c.dtype == "bf16"
+    tol = {"rel_l2": 1e-2, "max_abs": 5e-2} if bf16 else {"max_abs": 1e-4}
+    return {"tokens": int(n), "compared": int(ok.sum()), "near_tie_excluded": int((~ok).sum()),
+            "y_max_abs": mx, "y_rel_l2": rel, "tolerance": tol,
+            "within_tolerance": bool(mx <= tol["max_abs"] and (not bf16 or rel <= tol["rel_l2"]))}
+
+
+def library_record():
+    """Which libmoe.so this process loaded (path, size and hash of the file)."""
+    import hashlib
+
+    from sparse_mixture_experts_29_amd import binding
+    path = os.path.realpath(binding.LIB_PATH)
+    h = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    return {"path": os.path.relpath(path, ROOT) if path.startswith(ROOT) else path, "sha256_16": h,
+            "bytes": os.path.getsize(path), "moe_lib_override": bool(os.environ.get("MOE_LIB"))}
 
 
 def main():
@@ -488,7 +596,7 @@ def main():
 
     if args.workload in configs.SHARDS:
         return shard_bench(args, configs.SHARDS[args.workload])
-    cfg = configs.ALL[args.workload] if args.workload else configs.MIXTRAL_PREFILL
+    cfg = configs.ALL[args.workload] if args.workload else configs.DEEPSEEK_V3
     if args.backward:
         if args.cpu_tokens == 4096:
             args.cpu_tokens = 512
@@ -509,6 +617,8 @@ def main():
     counts = b["counts"].cpu().numpy()
     n_kept = int(b["offsets"][-1].item())
     touched = int((counts > 0).sum())
+    idx_g = b["idx"].cpu().numpy().astype(np.int64)
+    drop_g = b["drop"].cpu().numpy()
     del b
 
     if args.copy_mib:
@@ -606,6 +716,7 @@ def main():
             "max_over_mean_load": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
         },
         "clocks": clocks,
+        "library": library_record(),
     }
     if cfg.dtype == "bf16" and not small_batch:
         # both grouped launches (gate/up, down; shared experts ride in them as extra groups)
@@ -628,8 +739,13 @@ def main():
         out["graph"] = {"ms_per_step": round(float(g_ms.mean()), 4),
                         "value": round(cfg.T / (g_ms.mean() * 1e-3), 1),
                         "step_ms_p50": round(float(np.percentile(g_ms, 50)), 4)}
+    y_dev = dev.forward()
+    torch.cuda.synchronize()
+    out["routing"], oracle_routing = routing_telemetry(li, counts, drop_g, idx_g, n_kept)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(li, min(args.cpu_tokens, cfg.T))
+        out["cpu_baseline"], base_res, weights = cpu_baseline(li, min(args.cpu_tokens, cfg.T))
+        out["parity"] = parity_against_oracle(li, y_dev, idx_g, drop_g, base_res, weights, oracle_routing)
+        del base_res, weights
     print(json.dumps(out), flush=True)
 
 
