@@ -180,6 +180,24 @@ MOE_API moe_status moe_layer_forward(const moe_config* cfg, const void* x, const
                              const void* ws_down, void* y, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc. The intermediates live in a workspace the library owns: a static device buffer
+ * of MOE_STATIC_WORKSPACE_BYTES (64 MiB) on each GPU the library runs on, held until the
+ * process ends. The call allocates nothing (no hipMalloc, no allocating library routine).
+ * Layers whose moe_workspace_size(cfg, MOE_OP_LAYER) exceeds the buffer are refused with
+ * MOE_ERR_WORKSPACE before anything is enqueued; 64 MiB holds every batch of up to 64 tokens
+ * of the Mixtral-, Qwen3- and DeepSeek-V3-shaped layers, and a few hundred tokens of each.
+ * All calls on one GPU share that GPU's buffer: calls that overlap on one GPU (other
+ * streams, other host threads) race and give undefined results; serialise them. The buffer
+ * keeps the last call's contents; nothing in it needs to start at zero.
+ * Same arguments, results and errors as moe_layer_forward otherwise. */
+#define MOE_STATIC_WORKSPACE_BYTES (64u << 20)
+MOE_API moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router,
+                                     const float* router_bias, const void* w_gate, const void* w_up,
+                                     const void* w_down, const void* ws_gate, const void* ws_up,
+                                     const void* ws_down, void* y, void* stream);
+
 /* Expert-parallel shard (pages: shubhamtatvamasi.com/llm-inference/moe, section on serving
  * MoE across GPUs: each GPU holds a subset of the experts, token rows are dispatched to the
  * GPU that owns their expert and the expert outputs are sent back to be combined at home;

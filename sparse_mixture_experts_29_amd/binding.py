@@ -29,7 +29,7 @@ MOE_OP_PERMUTE, MOE_OP_GROUPED_MLP, MOE_OP_LAYER, MOE_OP_LAYER_BACKWARD = 0, 1, 
 # every function the header declares
 EXPORTS = ("moe_status_string", "moe_check_config", "moe_capacity", "moe_max_kept",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_mlp", "moe_combine",
-           "moe_layer_forward", "moe_expert_shard_forward", "moe_grouped_mlp_fp8",
+           "moe_layer_forward", "moe_layer_forward_noalloc", "moe_expert_shard_forward", "moe_grouped_mlp_fp8",
            "moe_layer_forward_fp8", "moe_layer_backward", "moe_time_next_launch")
 
 
@@ -95,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_grouped_mlp": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_combine": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P]),
         "moe_layer_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "moe_layer_forward_noalloc": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_expert_shard_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_grouped_mlp_fp8": (ctypes.c_int, [_C, _P, _P, _P, _F, _F, _P, _P, _P, sz, _P]),
         "moe_layer_forward_fp8": (ctypes.c_int, [_C, _P, _P, _P, _F, _F, _P, _P, sz, _P]),
@@ -205,6 +206,18 @@ def moe_layer_forward(cfg, x, w_router, router_bias, w_gate, w_up, w_down, ws_ga
         ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward")
+
+
+MOE_STATIC_WORKSPACE_BYTES = 64 << 20
+
+
+def moe_layer_forward_noalloc(cfg, x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+                              stream=None):
+    """moe_layer_forward with the library's own static workspace (calls on one GPU must not overlap)."""
+    _check(load_library().moe_layer_forward_noalloc(
+        ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y), _stream(stream)),
+        "moe_layer_forward_noalloc")
 
 
 def moe_expert_shard_forward(cfg, x_recv, local_expert, w_gate, w_up, w_down, y_send, ws, stream=None):

@@ -1,6 +1,7 @@
 // extern "C" entry points of libmoe: validation, workspace layout, launch sequence.
 // The computation itself is in router.hip, permute.hip, grouped_mlp.hip and combine.hip.
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 
@@ -235,6 +236,32 @@ moe_status fp8_args(const Shape& s, const moe_fp8_weights* experts, const moe_fp
   return MOE_OK;
 }
 
+// Library-owned workspace of moe_layer_forward_noalloc: one copy per GPU, held until the
+// process ends. Host code never uses the array's name as an address: the device address of
+// each GPU's copy is looked up once, with that device current, and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_WORKSPACE_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch` (hipGetSymbolAddress on first use on that device)
+hipError_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 TimingRequest& timing_request() {
@@ -400,6 +427,27 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   if (e == hipSuccess)
     e = launch_combine(s, w.y_perm, w.pos, w.gate, s.n_shared > 0 ? w.y_shared : nullptr, y, st);
   return hip_status(e);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router,
+                                     const float* router_bias, const void* w_gate, const void* w_up,
+                                     const void* w_down, const void* ws_gate, const void* ws_up,
+                                     const void* ws_down, void* y, void* stream) {
+  Shape s;
+  moe_status r = to_shape(cfg, &s);
+  if (r != MOE_OK) return r;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !y) return MOE_ERR_INVALID_ARG;
+  if (s.n_shared > 0 && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
+  // every check that needs no device comes first: a layer too large for the static buffer is
+  // refused before any HIP call
+  if (layer_layout(s, nullptr).bytes > static_cast<size_t>(MOE_STATIC_WORKSPACE_BYTES)) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (static_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+  // the layer's kernels need no part of the workspace zeroed: the persistent GEMM launches'
+  // tile counters are cleared by their own tile-table kernel on every call
+  return moe_layer_forward(cfg, x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y, ws,
+                           static_cast<size_t>(MOE_STATIC_WORKSPACE_BYTES), stream);
 }
 
 moe_status moe_expert_shard_forward(const moe_config* cfg, const void* x_recv, const int32_t* local_expert,
