@@ -198,6 +198,35 @@ MOE_API moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* 
                                      const void* w_down, const void* ws_gate, const void* ws_up,
                                      const void* ws_down, void* y, void* stream);
 
+/* Weights in the row-vector layout of y = x . W: the d x f matrices as the problem statement
+ * writes them (pages: shubhamtatvamasi.com/llm-inference/moe, section "The router": one linear
+ * layer maps the token's hidden vector to a logit per expert; klaylearn.com/glossary/
+ * mixture-of-experts, definition: each expert is a feed-forward block, run as a grouped GEMM
+ * over its batch). Device pointers, row-major, contiguous, element type cfg->dtype:
+ *   w_router [d][E]          w_gate, w_up [E][d][f]          w_down [E][f][d]
+ *   ws_gate, ws_up [n_shared][d][f_s]                        ws_down [n_shared][f_s][d]
+ * (the shared ones only when n_shared > 0). */
+typedef struct moe_rowvec_weights {
+  const void* w_router;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* ws_gate;
+  const void* ws_up;
+  const void* ws_down;
+} moe_rowvec_weights;
+
+/* One-time pack: writes the weights given in the row-vector layout into the layout every
+ * other entry point takes (each matrix transposed: w_router [E][d], w_gate, w_up [E][f][d],
+ * w_down [E][d][f], shared [n_shared][f_s][d] and [n_shared][d][f_s]), in buffers the caller
+ * owns and then passes to the layer calls. Bit-exact (elements are moved, never rounded).
+ * cfg->T is ignored. Sources and destinations must not overlap; all routed pointers are
+ * required, the shared ones iff n_shared > 0 (MOE_ERR_INVALID_ARG otherwise). Memory-bound:
+ * each weight byte is read and written once. */
+MOE_API moe_status moe_pack_weights(const moe_config* cfg, const moe_rowvec_weights* src, void* w_router,
+                            void* w_gate, void* w_up, void* w_down, void* ws_gate, void* ws_up,
+                            void* ws_down, void* stream);
+
 /* Expert-parallel shard (pages: shubhamtatvamasi.com/llm-inference/moe, section on serving
  * MoE across GPUs: each GPU holds a subset of the experts, token rows are dispatched to the
  * GPU that owns their expert and the expert outputs are sent back to be combined at home;

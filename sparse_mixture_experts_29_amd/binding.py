@@ -29,7 +29,7 @@ MOE_OP_PERMUTE, MOE_OP_GROUPED_MLP, MOE_OP_LAYER, MOE_OP_LAYER_BACKWARD = 0, 1, 
 # every function the header declares
 EXPORTS = ("moe_status_string", "moe_check_config", "moe_capacity", "moe_max_kept",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_mlp", "moe_combine",
-           "moe_layer_forward", "moe_layer_forward_noalloc", "moe_expert_shard_forward", "moe_grouped_mlp_fp8",
+           "moe_layer_forward", "moe_layer_forward_noalloc", "moe_pack_weights", "moe_expert_shard_forward", "moe_grouped_mlp_fp8",
            "moe_layer_forward_fp8", "moe_layer_backward", "moe_time_next_launch")
 
 
@@ -58,6 +58,14 @@ class MoeFp8Weights(ctypes.Structure):
                 ("scale_down", ctypes.c_void_p)]
 
 
+class MoeRowvecWeights(ctypes.Structure):
+    """moe_rowvec_weights: weights in the row-vector layout of y = x . W (device pointers):
+    router [d][E], gate/up [E][d][f], down [E][f][d], shared [n_s][d][f_s] and [n_s][f_s][d]."""
+    _fields_ = [("w_router", ctypes.c_void_p), ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("ws_gate", ctypes.c_void_p), ("ws_up", ctypes.c_void_p),
+                ("ws_down", ctypes.c_void_p)]
+
+
 class MoeLayerGrads(ctypes.Structure):
     """moe_layer_grads: device pointers of the gradients moe_layer_backward writes."""
     _fields_ = [("dx", ctypes.c_void_p), ("dw_router", ctypes.c_void_p), ("d_router_bias", ctypes.c_void_p),
@@ -71,6 +79,7 @@ _P = ctypes.c_void_p
 _C = ctypes.POINTER(MoeConfig)
 _F = ctypes.POINTER(MoeFp8Weights)
 _G = ctypes.POINTER(MoeLayerGrads)
+_W = ctypes.POINTER(MoeRowvecWeights)
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -96,6 +105,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P]),
         "moe_layer_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_layer_forward_noalloc": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_pack_weights": (ctypes.c_int, [_C, _W, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_expert_shard_forward": (ctypes.c_int, [_C, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_grouped_mlp_fp8": (ctypes.c_int, [_C, _P, _P, _P, _F, _F, _P, _P, _P, sz, _P]),
         "moe_layer_forward_fp8": (ctypes.c_int, [_C, _P, _P, _P, _F, _F, _P, _P, sz, _P]),
@@ -218,6 +228,16 @@ def moe_layer_forward_noalloc(cfg, x, w_router, router_bias, w_gate, w_up, w_dow
         ctypes.byref(_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y), _stream(stream)),
         "moe_layer_forward_noalloc")
+
+
+def moe_pack_weights(cfg, src, w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None,
+                     stream=None):
+    """src: the seven row-vector-layout tensors (router, gate, up, down, shared gate, up, down;
+    the shared ones None without shared experts); the rest: the packed outputs."""
+    sw = MoeRowvecWeights(*[_ptr(t) for t in src])
+    _check(load_library().moe_pack_weights(
+        ctypes.byref(_cfg(cfg)), ctypes.byref(sw), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _stream(stream)), "moe_pack_weights")
 
 
 def moe_expert_shard_forward(cfg, x_recv, local_expert, w_gate, w_up, w_down, y_send, ws, stream=None):

@@ -450,6 +450,30 @@ moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const
                            static_cast<size_t>(MOE_STATIC_WORKSPACE_BYTES), stream);
 }
 
+moe_status moe_pack_weights(const moe_config* cfg, const moe_rowvec_weights* src, void* w_router, void* w_gate,
+                            void* w_up, void* w_down, void* ws_gate, void* ws_up, void* ws_down, void* stream) {
+  Shape s;
+  moe_status r = to_shape(cfg, &s);
+  if (r != MOE_OK) return r;
+  if (!src || !src->w_router || !src->w_gate || !src->w_up || !src->w_down) return MOE_ERR_INVALID_ARG;
+  if (!w_router || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARG;
+  if (s.n_shared > 0 && (!src->ws_gate || !src->ws_up || !src->ws_down || !ws_gate || !ws_up || !ws_down))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int eb = static_cast<int>(es(s));
+  // [d][E] -> [E][d]; [E][d][f] -> [E][f][d]; [E][f][d] -> [E][d][f]
+  hipError_t e = launch_transpose_batched(src->w_router, w_router, 1, s.d, s.E, eb, st);
+  if (e == hipSuccess) e = launch_transpose_batched(src->w_gate, w_gate, s.E, s.d, s.f, eb, st);
+  if (e == hipSuccess) e = launch_transpose_batched(src->w_up, w_up, s.E, s.d, s.f, eb, st);
+  if (e == hipSuccess) e = launch_transpose_batched(src->w_down, w_down, s.E, s.f, s.d, eb, st);
+  if (s.n_shared > 0) {
+    if (e == hipSuccess) e = launch_transpose_batched(src->ws_gate, ws_gate, s.n_shared, s.d, s.f_s, eb, st);
+    if (e == hipSuccess) e = launch_transpose_batched(src->ws_up, ws_up, s.n_shared, s.d, s.f_s, eb, st);
+    if (e == hipSuccess) e = launch_transpose_batched(src->ws_down, ws_down, s.n_shared, s.f_s, s.d, eb, st);
+  }
+  return hip_status(e);
+}
+
 moe_status moe_expert_shard_forward(const moe_config* cfg, const void* x_recv, const int32_t* local_expert,
                                     const void* w_gate, const void* w_up, const void* w_down, void* y_send,
                                     void* ws, size_t ws_bytes, void* stream) {

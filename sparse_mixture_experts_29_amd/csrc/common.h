@@ -191,6 +191,11 @@ hipError_t launch_fma_gemm(const float* A, int64_t sam, int64_t sak, const void*
                            int64_t K, void* C, int64_t ldc, float* partials, hipStream_t st);
 hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st);
 
+// Weight pack (pack.hip): dst[b][c][r] = src[b][r][c] for `batch` R x C matrices of 2- or
+// 4-byte elements.
+hipError_t launch_transpose_batched(const void* src, void* dst, int64_t batch, int R, int C, int elem_bytes,
+                                    hipStream_t st);
+
 struct TimingRequest {
   int kernel = -1;
   hipEvent_t begin = nullptr, end = nullptr;
