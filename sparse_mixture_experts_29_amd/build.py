@@ -1,8 +1,10 @@
 """Build libmoe.so (gfx950) in-tree: one hipcc compile per source, then a shared link.
 
-    python -m sparse_mixture_experts_29_amd.build [--jobs N]
+    python -m sparse_mixture_experts_29_amd.build [--jobs N] [--out PATH] [-D NAME=VALUE ...]
 
-Every source is compiled every time (the build check must compile, not reuse).
+Every source is compiled every time (the build check must compile, not reuse). --out and -D
+build a variant of the same sources elsewhere (tuning macros such as MOE_GEMM_*), which the
+binding loads when MOE_LIB names it; the in-tree library is unchanged by such a build.
 """
 from __future__ import annotations
 
@@ -41,33 +43,38 @@ def _run(cmd):
     return err
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
+def build(jobs: int = 8, verbose: bool = False, out: str = OUT, defines=()) -> str:
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    # a variant build keeps its objects apart from the in-tree ones
+    bdir = BUILD if out == OUT else os.path.join(BUILD, "variant_" + os.path.basename(out).replace(".", "_"))
+    os.makedirs(bdir, exist_ok=True)
     objs = []
+    dflags = [f"-D{d}" for d in defines]
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        msg = _run([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
+        msg = _run([HIPCC, *CFLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and msg:
             print(msg, file=sys.stderr)
         return obj
 
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--out", default=OUT, help="where to write the library (default: in-tree)")
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra preprocessor define NAME=VALUE")
     a = ap.parse_args()
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, os.path.abspath(a.out), a.defines))
 
 
 if __name__ == "__main__":
