@@ -14,7 +14,7 @@
 // The bf16 K loop reads 32 contiguous bytes per lane per operand per 64-wide K block and
 // feeds them to 2 MFMAs; the MFMA sees a permuted K order, identical for both operands, so
 // the dot products are unchanged.
-#include "permute_block.h"
+#include "common.h"
 
 namespace moe {
 namespace {
@@ -550,7 +550,7 @@ template <typename T, int EMAX, int TB>
 __device__ __forceinline__ void router_small_e_block(
     const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
     int32_t* __restrict__ idx, float* __restrict__ gate, float* __restrict__ logits, int n_tok,
-    int d, int E, int k, int gating, int blk) {
+    int d, int E, int k, int gating, int blk, int* sidx = nullptr) {
   static_assert(TB * EMAX == 32, "32 partial sums per lane");
   __shared__ float part[256][33];  // +1: rows fall on distinct banks
   __shared__ float red[8][32];
@@ -644,7 +644,53 @@ __device__ __forceinline__ void router_small_e_block(
   if (lane < k) {
     idx[static_cast<int64_t>(t) * k + lane] = mine_e;
     gate[static_cast<int64_t>(t) * k + lane] = p / sum;
+    if (sidx) sidx[wave * k + lane] = mine_e;  // the block's pairs, for a permute in the same block
   }
+}
+
+// Permute of at most 64 pairs (a decode batch routed by this block) by one wave: ex = the
+// pairs' experts from LDS (pair s = lane). Lane e < E counts expert e's pairs, a wave prefix
+// sum of the capped counts gives the offsets, and a pair's rank within its expert is the
+// number of lower pairs with the same expert: the order (expert, then pair, i.e. token)
+// and the drops (the highest tokens beyond the capacity) of the block permute. E <= 63.
+__device__ __forceinline__ void permute_tiny_wave(const int* sidx, int n_pairs, int E, int64_t capacity,
+                                                  int64_t max_kept, int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+                                                  int32_t* __restrict__ pos, uint8_t* __restrict__ drop) {
+  const int lane = threadIdx.x & 63;
+  int e = lane < n_pairs ? sidx[lane] : -1;
+  if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) e = -1;  // outside [0, E): dropped
+  int cnt = 0, rank = 0;
+  for (int j = 0; j < n_pairs; ++j) {
+    const int ej = __shfl(e, j);
+    cnt += ej == lane;
+    rank += (j < lane && ej == e) ? 1 : 0;
+  }
+  const int kept = lane < E ? (capacity >= 0 && cnt > capacity ? static_cast<int>(capacity) : cnt) : 0;
+  int incl = kept;  // inclusive prefix over the lanes
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  const int off = incl - kept;
+  const int n_kept = __shfl(incl, 63);
+  if (lane < E) {
+    counts[lane] = cnt;
+    offsets[lane] = off;
+  }
+  if (lane == 0) offsets[E] = n_kept;
+  const int base = __shfl(off, e < 0 ? 0 : e);
+  if (lane < n_pairs) {
+    if (e >= 0 && (capacity < 0 || rank < capacity)) {
+      sorted_slot[base + rank] = lane;
+      pos[lane] = base + rank;
+      drop[lane] = 0;
+    } else {
+      pos[lane] = -1;
+      drop[lane] = 1;
+    }
+  }
+  for (int64_t q = n_kept + lane; q < max_kept; q += 64) sorted_slot[q] = -1;
 }
 
 
@@ -657,22 +703,23 @@ __global__ __launch_bounds__(256) void router_small_e_kernel(
 }
 
 // Route and permute in one launch when both fit one block (the router's single block of TB
-// tokens, at most kPermuteChunk pairs): the block's top-k writes reach global memory, the
-// barrier makes them visible to the whole block, and the block then runs the one-block
-// permute on them. Saves a launch and its gap on decode steps; the results are those of the
-// two separate launches.
+// tokens, at most 32 pairs): the block's top-k choices are also kept in LDS, and after a
+// barrier one wave permutes them (permute_tiny_wave). Saves a launch and its gap on decode
+// steps, and the one-block permute's scan and its global round trip of the choices (about
+// 2 us a step, measured at T = 1 and 4); the results are those of the two separate launches.
 template <typename T, int EMAX, int TB>
 __global__ __launch_bounds__(256) void route_permute_single_kernel(
     const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
     int32_t* __restrict__ idx, float* __restrict__ gate, float* __restrict__ logits, int n_tok,
-    int d, int E, int k, int gating, int ebits, int64_t capacity, int64_t max_kept,
+    int d, int E, int k, int gating, int64_t capacity, int64_t max_kept,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ pos, uint8_t* __restrict__ drop) {
-  __shared__ int plds[permute_block_lds_ints(EMAX)];
-  router_small_e_block<T, EMAX, TB>(x, w, bias, idx, gate, logits, n_tok, d, E, k, gating, 0);
+  // the pairs (at most TB * k <= 32) stay in LDS; one wave permutes them
+  __shared__ int sidx[64];
+  router_small_e_block<T, EMAX, TB>(x, w, bias, idx, gate, logits, n_tok, d, E, k, gating, 0, sidx);
   __syncthreads();
-  permute_single_block(idx, static_cast<int64_t>(n_tok) * k, E, ebits, capacity, max_kept, counts, offsets,
-                       sorted_slot, pos, drop, plds);
+  if (threadIdx.x < 64)
+    permute_tiny_wave(sidx, n_tok * k, E, capacity, max_kept, counts, offsets, sorted_slot, pos, drop);
 }
 }  // namespace
 
@@ -760,19 +807,17 @@ hipError_t launch_route_permute(const Shape& s, const void* x, const void* w_rou
     if (e == hipSuccess) e = launch_permute(s, idx, counts, offsets, sorted_slot, pos, drop, permute_ws, st);
     return e;
   }
-  int ebits = 0;
-  while ((1 << ebits) < s.E) ++ebits;
   timing_begin(MOE_KERNEL_ROUTER, st);
   const dim3 g(1), b(kRouterThreads);
   if (s.dtype == MOE_BF16) {
     auto kern = e8 ? route_permute_single_kernel<bf16_t, 8, 4> : route_permute_single_kernel<bf16_t, 32, 1>;
     hipLaunchKernelGGL(kern, g, b, 0, st, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_router), bias,
-                       idx, gate, logits, T, s.d, s.E, s.k, s.gating, ebits, s.capacity, s.max_kept, counts, offsets,
+                       idx, gate, logits, T, s.d, s.E, s.k, s.gating, s.capacity, s.max_kept, counts, offsets,
                        sorted_slot, pos, drop);
   } else {
     auto kern = e8 ? route_permute_single_kernel<float, 8, 4> : route_permute_single_kernel<float, 32, 1>;
     hipLaunchKernelGGL(kern, g, b, 0, st, static_cast<const float*>(x), static_cast<const float*>(w_router), bias,
-                       idx, gate, logits, T, s.d, s.E, s.k, s.gating, ebits, s.capacity, s.max_kept, counts, offsets,
+                       idx, gate, logits, T, s.d, s.E, s.k, s.gating, s.capacity, s.max_kept, counts, offsets,
                        sorted_slot, pos, drop);
   }
   timing_end(MOE_KERNEL_ROUTER, st);
