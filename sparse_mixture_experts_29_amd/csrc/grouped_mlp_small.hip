@@ -559,13 +559,17 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   a.N_s = s.f_s;
   a.K_s = s.d;
   const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
-  // FP8 weights with two token groups per wave: two chunks per wave, so each token-row
-  // fragment feeds both (the token-row reads, twice the FP8 weight bytes at one chunk, halve;
-  // measured on the Mixtral-shaped T = 64 layer: gated 245 -> 203 us, down 168 -> 126 us). The
-  // K splits are chosen on 16-column chunks either way.
+  // FP8 weights: two 16-row chunks per wave, so each token-row fragment feeds both and the
+  // token-row reads from L2 per code byte halve. The gated launch takes them with two token
+  // groups per wave (T > 16; at one group halving the units costs more than it saves), the
+  // down launch always. Measured on the Mixtral-shaped layer (A/B builds, one box): T = 64
+  // gated 245 -> 203 us and down 168 -> 126 us; down T = 16 104 -> 87 us, T = 1 28 -> 25 us;
+  // the gated launch at T <= 16 and every bf16 launch lose with two chunks. The K splits are
+  // chosen on 16-column chunks either way.
   const int groups16 = static_cast<int>((s.T + 15) / 16);
-  const int cpw = f8 && groups16 > 1 ? 2 : 1;
-  a.n_chunks = fmax / (16 * cpw);
+  const int cpw_g = f8 && groups16 > 1 ? 2 : 1;
+  const int cpw_d = f8 ? 2 : 1;
+  a.n_chunks = fmax / (16 * cpw_g);
   a.splits = small_m_splits(s, true);
   a.fw = fmax;
   a.part = part;
@@ -574,10 +578,9 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   const int ngw = groups16 <= 1 ? 1 : 2;
   a.halves = (groups16 + ngw - 1) / ngw;
   auto kern_g = f8 ? (ngw == 1 ? small_m_kernel<true, 1, true>
-                                : (cpw == 2 ? small_m_kernel<true, 2, true, 2> : small_m_kernel<true, 2, true>))
+                                : (cpw_g == 2 ? small_m_kernel<true, 2, true, 2> : small_m_kernel<true, 2, true>))
                   : (ngw == 1 ? small_m_kernel<true, 1, false> : small_m_kernel<true, 2, false>);
-  auto kern_d = f8 ? (ngw == 1 ? small_m_kernel<false, 1, true>
-                                : (cpw == 2 ? small_m_kernel<false, 2, true, 2> : small_m_kernel<false, 2, true>))
+  auto kern_d = f8 ? (ngw == 1 ? small_m_kernel<false, 1, true, 2> : small_m_kernel<false, 2, true, 2>)
                   : (ngw == 1 ? small_m_kernel<false, 1, false> : small_m_kernel<false, 2, false>);
   a.s0_r = fp8.gate;
   a.s1_r = fp8.up;
@@ -611,7 +614,7 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   a.K_r = s.f;
   a.N_s = s.d;
   a.K_s = s.f_s;
-  a.n_chunks = s.d / (16 * cpw);
+  a.n_chunks = s.d / (16 * cpw_d);
   a.splits = small_m_splits(s, false);
   units = static_cast<int64_t>(G) * a.n_chunks * a.splits * a.halves;
   timing_begin(MOE_KERNEL_DOWN, st);
