@@ -182,8 +182,14 @@ def sample_clocks(step, want: int = 2, seconds: float = 8.0) -> dict:
                 got = {}
                 for card in json.loads(r.stdout).values():  # every card-like entry
                     if isinstance(card, dict):
-                        got.update({k.split(" clock")[0].strip(): str(v).strip("()") for k, v in card.items()
-                                    if "clk" in k.lower() or "clock" in k.lower()})
+                        # "<clk> clock speed:" holds the frequency, "<clk> clock level:" the DPM
+                        # level; keep both under distinct names
+                        for key, v in card.items():
+                            kl = key.lower()
+                            if "clk" not in kl and "clock" not in kl:
+                                continue
+                            name = key.split(" clock")[0].strip() + ("_level" if "level" in kl else "")
+                            got[name] = str(v).strip("()")
                 if not got:
                     errors.append("no clock fields in: " + r.stdout[:200])
                     return

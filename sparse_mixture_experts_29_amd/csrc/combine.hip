@@ -97,20 +97,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 // bf16 and widened back (the value the ordered reduction stores into y_perm).
 __device__ __forceinline__ void split_sum_bf16(const float* __restrict__ part, int64_t row, int64_t rows_total,
                                                int d, int c, int splits, float* v) {
-  float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
-  for (int sp = 0; sp < splits; ++sp) {
-    const float* pp = part + (static_cast<int64_t>(sp) * rows_total + row) * d + c * 8;
-    const float4 a = *reinterpret_cast<const float4*>(pp);
-    const float4 b = *reinterpret_cast<const float4*>(pp + 4);
-    s0.x += a.x;
-    s0.y += a.y;
-    s0.z += a.z;
-    s0.w += a.w;
-    s1.x += b.x;
-    s1.y += b.y;
-    s1.z += b.z;
-    s1.w += b.w;
-  }
+  float4 s0, s1;
+  split_sum2(part + row * d + c * 8, rows_total * d, 4, splits, s0, s1);
   const uint32_t w[4] = {pack_bf16x2(s0.x, s0.y), pack_bf16x2(s0.z, s0.w), pack_bf16x2(s1.x, s1.y),
                          pack_bf16x2(s1.z, s1.w)};
 #pragma unroll

@@ -39,6 +39,39 @@ __device__ __forceinline__ float silu_f32(float g) {
 
 __device__ __forceinline__ float sigmoid_f32(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
+// Sums over K splits, in split order from zero, of the float4 at p and the one at p + off2 in
+// every split's slice (slices `stride` floats apart). The loads of up to 8 splits are issued
+// before any of them is added: split-K partials are written by waves on other XCDs, so every
+// load goes past this XCD's L2, and a small batch's reduction otherwise waits on a chain of
+// such round trips, one per split.
+__device__ __forceinline__ void split_sum2(const float* __restrict__ p, int64_t stride, int64_t off2, int splits,
+                                           float4& s0, float4& s1) {
+  s0 = make_float4(0.f, 0.f, 0.f, 0.f);
+  s1 = s0;
+  for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+    float4 a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (sp0 + u < splits) {
+        const float* q = p + static_cast<int64_t>(sp0 + u) * stride;
+        a[u] = *reinterpret_cast<const float4*>(q);
+        b[u] = *reinterpret_cast<const float4*>(q + off2);
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (sp0 + u < splits) {
+        s0.x += a[u].x;
+        s0.y += a[u].y;
+        s0.z += a[u].z;
+        s0.w += a[u].w;
+        s1.x += b[u].x;
+        s1.y += b[u].y;
+        s1.z += b[u].z;
+        s1.w += b[u].w;
+      }
+  }
+}
+
 // Internal view of moe_config with derived quantities (host-computed).
 struct Shape {
   int64_t T;

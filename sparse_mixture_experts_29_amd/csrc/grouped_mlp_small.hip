@@ -427,20 +427,8 @@ __global__ __launch_bounds__(256) void small_m_swiglu_reduce(const float* __rest
   const int c = static_cast<int>(i % cq) * 4;
   const bool routed = row < max_kept;
   if (routed ? (row >= offsets[E] || c >= f) : c >= f_s) return;
-  float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
-  for (int sp = 0; sp < splits; ++sp) {
-    const float* pp = part + (static_cast<int64_t>(sp) * rows_total + row) * 2 * fw + c;
-    const float4 vg = *reinterpret_cast<const float4*>(pp);
-    const float4 vu = *reinterpret_cast<const float4*>(pp + fw);
-    g.x += vg.x;
-    g.y += vg.y;
-    g.z += vg.z;
-    g.w += vg.w;
-    u.x += vu.x;
-    u.y += vu.y;
-    u.z += vu.z;
-    u.w += vu.w;
-  }
+  float4 g, u;
+  split_sum2(part + row * 2 * fw + c, rows_total * 2 * fw, fw, splits, g, u);
   bf16_t* op = routed ? h + row * f + c : hs + (row - max_kept) * f_s + c;
   uint2 pk;
   pk.x = pack_bf16x2(silu_f32(g.x) * u.x, silu_f32(g.y) * u.y);
@@ -449,32 +437,28 @@ __global__ __launch_bounds__(256) void small_m_swiglu_reduce(const float* __rest
 }
 
 // y = sum over splits of the partials, in split order, rounded once to bf16.
-// One thread per 4 consecutive columns of one row; routed rows past N_kept are skipped.
+// One thread per 8 consecutive columns of one row; routed rows past N_kept are skipped.
 __global__ __launch_bounds__(256) void small_m_reduce(const float* __restrict__ part,
                                                       const int32_t* __restrict__ offsets, int E,
                                                       int64_t max_kept, int n_shared, int T, int N,
                                                       int splits, bf16_t* __restrict__ y_perm,
                                                       bf16_t* __restrict__ y_shared) {
   const int64_t rows_total = max_kept + static_cast<int64_t>(n_shared) * T;
-  const int cq = N / 4;
+  const int co = N / 8;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= rows_total * cq) return;
-  const int64_t row = i / cq;
-  const int c = static_cast<int>(i % cq) * 4;
+  if (i >= rows_total * co) return;
+  const int64_t row = i / co;
+  const int c = static_cast<int>(i % co) * 8;
   if (row < max_kept && row >= offsets[E]) return;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = 0; sp < splits; ++sp) {
-    const float4 v = *reinterpret_cast<const float4*>(part + (static_cast<int64_t>(sp) * rows_total + row) * N + c);
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
-  }
+  float4 s0, s1;
+  split_sum2(part + row * N + c, rows_total * N, 4, splits, s0, s1);
   bf16_t* op = row < max_kept ? y_perm + row * N + c : y_shared + (row - max_kept) * N + c;
-  uint2 pk;
-  pk.x = pack_bf16x2(s.x, s.y);
-  pk.y = pack_bf16x2(s.z, s.w);
-  *reinterpret_cast<uint2*>(op) = pk;
+  uint4 pk;
+  pk.x = pack_bf16x2(s0.x, s0.y);
+  pk.y = pack_bf16x2(s0.z, s0.w);
+  pk.z = pack_bf16x2(s1.x, s1.y);
+  pk.w = pack_bf16x2(s1.z, s1.w);
+  *reinterpret_cast<uint4*>(op) = pk;
 }
 
 int max_groups(const Shape& s) {
@@ -491,7 +475,7 @@ bool use_small_m(const Shape& s) {
 hipError_t launch_split_reduce(const Shape& s, const float* part, int splits, const int32_t* offsets, void* y_perm,
                                void* y_shared, hipStream_t st) {
   const int64_t rows_total = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
-  const int64_t threads = rows_total * (s.d / 4);
+  const int64_t threads = rows_total * (s.d / 8);
   hipLaunchKernelGGL(small_m_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st, part,
                      offsets, s.E, s.max_kept, s.n_shared, static_cast<int>(s.T), s.d, splits,
                      static_cast<bf16_t*>(y_perm), static_cast<bf16_t*>(y_shared));
@@ -621,7 +605,7 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   hipLaunchKernelGGL(kern_d, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(kThreads), 0, st, a);
   timing_end(MOE_KERNEL_DOWN, st);
   if (y_perm == nullptr) return hipGetLastError();  // the caller combines from the partials
-  const int64_t threads = rows_total * (s.d / 4);
+  const int64_t threads = rows_total * (s.d / 8);
   hipLaunchKernelGGL(small_m_reduce, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st, part,
                      offsets, s.E, s.max_kept, s.n_shared, static_cast<int>(s.T), s.d, a.splits,
                      static_cast<bf16_t*>(y_perm), static_cast<bf16_t*>(y_shared));

@@ -580,29 +580,42 @@ __device__ __forceinline__ void router_small_e_block(
       for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(r[i / 4][i % 4]);
     }
   };
-  // d is a multiple of 64, so a lane's 8 elements never straddle the end
-  for (int c = threadIdx.x * 8; c < d; c += 2048) {
-    u32x4 xr_raw[TB][kVec], wr_raw[EMAX][kVec];
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-#pragma unroll
-      for (int q = 0; q < kVec; ++q) xr_raw[b][q] = *reinterpret_cast<const u32x4*>(xr[b] + c + 4 * q);
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e)
-#pragma unroll
-      for (int q = 0; q < kVec; ++q) wr_raw[e][q] = *reinterpret_cast<const u32x4*>(wr[e] + c + 4 * q);
+  // d is a multiple of 64, so a lane's 8 elements never straddle the end. With few rows per
+  // pass (E <= 8, bf16), two passes of the block (4096 elements) are loaded before either is
+  // multiplied: at decode batch sizes the block's time is the latency of its load rounds.
+  constexpr int NP = (TB + EMAX) * kVec <= 12 ? 2 : 1;
+  auto fma_pass = [&](const u32x4 (&xraw)[TB][kVec], const u32x4 (&wraw)[EMAX][kVec]) {
     float xv[TB][8];
 #pragma unroll
-    for (int b = 0; b < TB; ++b) widen(xr_raw[b], xv[b]);
+    for (int b = 0; b < TB; ++b) widen(xraw[b], xv[b]);
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
       float wv[8];
-      widen(wr_raw[e], wv);
+      widen(wraw[e], wv);
 #pragma unroll
       for (int b = 0; b < TB; ++b)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[b * EMAX + e] = fmaf(xv[b][i], wv[i], acc[b * EMAX + e]);
     }
+  };
+  for (int c = threadIdx.x * 8; c < d; c += NP * 2048) {
+    u32x4 xr_raw[NP][TB][kVec], wr_raw[NP][EMAX][kVec];
+#pragma unroll
+    for (int h = 0; h < NP; ++h) {
+      const int ch = c + h * 2048;
+      if (ch >= d) break;
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) xr_raw[h][b][q] = *reinterpret_cast<const u32x4*>(xr[b] + ch + 4 * q);
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) wr_raw[h][e][q] = *reinterpret_cast<const u32x4*>(wr[e] + ch + 4 * q);
+    }
+#pragma unroll
+    for (int h = 0; h < NP; ++h)
+      if (c + h * 2048 < d) fma_pass(xr_raw[h], wr_raw[h]);
   }
 #pragma unroll
   for (int i = 0; i < 32; ++i) part[threadIdx.x][i] = acc[i];
