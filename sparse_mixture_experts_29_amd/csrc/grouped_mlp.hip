@@ -356,6 +356,162 @@ __device__ __forceinline__ void kloop_pipelined(f32x16 (&acc)[4][LIVE > 0 ? LIVE
 }
 static_assert(IPW == 8 || BK != 32, "the pipelined loop issues 8 DMA instructions per stage");
 
+// Software-pipelined K loop for stages of BK = 64 (LDS rows of 128 bytes, so every DMA
+// instruction fetches whole 128-byte lines, 8 rows each, and a stage takes 16 instructions a
+// wave) in a ring of two stages. Per stage kt, four k-steps of NM = 4*LIVE MFMAs, operand
+// fragments alternating between two register sets:
+//   A: k-step 0 (set 0) | reads of k-step 1 (set 1), DMA instructions ND..15 of stage kt+1
+//   B: k-step 1 (set 1) | reads of k-step 2 (set 0)
+//   C: k-step 2 (set 0) | reads of k-step 3 (set 1)
+//   -- wait for this wave's LDS reads and for all of stage kt+1's DMA, workgroup barrier --
+//   D: k-step 3 (set 1) | reads of stage kt+1's k-step 0 (set 0), DMA instructions 0..ND-1
+//      of stage kt+2 into the slot of stage kt, which every wave has finished reading
+// Stage kt+2 is thus issued over D of stage kt and A of stage kt+1 and waited for at the
+// barrier of stage kt+1. Both slots are filled in the prologue. Every wave passes one barrier
+// per stage but the last, whatever its LIVE.
+template <int LIVE>
+__device__ __forceinline__ void kloop_wide(f32x16 (&acc)[4][LIVE > 0 ? LIVE : 1], bf16_t* lds,
+                                           const DmaPlan& dp, int K, int wave,
+                                           const int (&aoff)[4], const int (&boff)[LIVE > 0 ? LIVE : 1],
+                                           int swz_l, int khalf) {
+  static_assert(BK == 64 && NST == 2 && IPW == 16, "stages of 64, two of them, 16 DMA instructions a wave");
+  constexpr int STAGE = (BW + 256) * BK;
+  constexpr int NB = LIVE > 0 ? LIVE : 1;
+  constexpr int NM = 4 * LIVE;             // MFMAs per k-step
+  constexpr int NR = LIVE ? 4 + LIVE : 0;  // LDS reads per k-step
+#ifndef MOE_WIDE_DMA_D
+#define MOE_WIDE_DMA_D 8
+#endif
+  constexpr int ND = MOE_WIDE_DMA_D;       // DMA instructions of stage kt+2 issued in D
+  constexpr int NA = IPW - ND;             // the rest, issued in A of the next stage
+  constexpr int NMR = NM > NR ? NM : NR;
+  // a phase's DMA instructions spread evenly over its MFMA slots: one every SA (SD) slots
+  constexpr int SA = NA == 0 || NA >= NMR ? 1 : NMR / NA;
+  constexpr int SD = ND == 0 || ND >= NMR ? 1 : NMR / ND;
+  constexpr int LA = NMR > NA * SA ? NMR : NA * SA;  // slots of phase A when it issues DMA
+  constexpr int LD = NMR > ND * SD ? NMR : ND * SD;
+  const int KT = K / BK;
+  bf16x8 fa0[4], fb0[NB], fa1[4], fb1[NB];
+  auto rd = [&](const bf16_t* st, int kk, int idx, bf16x8 (&fa)[4], bf16x8 (&fb)[NB]) {
+    const int c = ((kk * 2 + khalf) ^ swz_l) << 3;
+    if (idx < 4)
+      fa[idx] = *reinterpret_cast<const bf16x8*>(st + aoff[idx] + c);
+    else
+      fb[idx - 4] = *reinterpret_cast<const bf16x8*>(st + boff[idx - 4] + c);
+  };
+  auto mf = [&](int m, const bf16x8 (&fa)[4], const bf16x8 (&fb)[NB]) {
+    const int i = m & 3, j = m >> 2;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  auto sb = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto dma = [&](int st, int i) {
+    bf16_t* dst = lds + (st & 1) * STAGE + wave * 128 * BK;
+    const uint32_t kb = static_cast<uint32_t>(st) * BK * 2u;
+    __builtin_amdgcn_global_load_lds(dp.base + dp.off[i] + kb, (lds_void*)(dst + i * RPI * BK), 16, 0, 0);
+  };
+
+  // prologue: both slots filled, wait for stage 0, read its k-step 0 operands
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) dma(0, i);
+  if (KT > 1) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) dma(1, i);
+    wait_vmcnt<IPW>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  stage_barrier();
+#pragma unroll
+  for (int r = 0; r < NR; ++r) rd(lds, 0, r, fa0, fb0);
+  sb();
+
+  // A_ON: A issues the second half of stage kt+1; D_ON: D issues the first half of stage kt+2;
+  // NEXT: the barrier and the reads of stage kt+1 (every stage but the last)
+  auto stage_step = [&](int kt, auto a_on, auto d_on, auto next_on) {
+    constexpr bool A_ON = decltype(a_on)::value;
+    constexpr bool D_ON = decltype(d_on)::value;
+    constexpr bool NEXT = decltype(next_on)::value;
+    const bf16_t* cur = lds + (kt & 1) * STAGE;
+    // A: a DMA instruction after every second MFMA slot
+#pragma unroll
+    for (int m = 0; m < (A_ON ? LA : NMR); ++m) {
+      if (m < NM) {
+        mf(m, fa0, fb0);
+        sb();
+      }
+      if (m < NR) {
+        rd(cur, 1, m, fa1, fb1);
+        sb();
+      }
+      if (A_ON && m % SA == SA - 1 && m / SA < NA) {
+        dma(kt + 1, ND + m / SA);
+        sb();
+      }
+    }
+    // B
+#pragma unroll
+    for (int m = 0; m < NMR; ++m) {
+      if (m < NM) {
+        mf(m, fa1, fb1);
+        sb();
+      }
+      if (m < NR) {
+        rd(cur, 2, m, fa0, fb0);
+        sb();
+      }
+    }
+    // C
+#pragma unroll
+    for (int m = 0; m < NMR; ++m) {
+      if (m < NM) {
+        mf(m, fa0, fb0);
+        sb();
+      }
+      if (m < NR) {
+        rd(cur, 3, m, fa1, fb1);
+        sb();
+      }
+    }
+    if (NEXT) {
+      wait_lgkmcnt0();
+      wait_vmcnt<0>();
+      stage_barrier();
+    }
+    // D: a DMA instruction before every second MFMA slot
+    const bf16_t* nxt = lds + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+    for (int m = 0; m < (D_ON ? LD : NMR); ++m) {
+      if (D_ON && m % SD == 0 && m / SD < ND) {
+        dma(kt + 2, m / SD);
+        sb();
+      }
+      if (m < NM) {
+        mf(m, fa1, fb1);
+        sb();
+      }
+      if (NEXT && m < NR) {
+        rd(nxt, 0, m, fa0, fb0);
+        sb();
+      }
+    }
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  if (KT >= 3)
+    stage_step(0, no{}, yes{}, yes{});
+  else if (KT == 2)
+    stage_step(0, no{}, no{}, yes{});
+  else
+    stage_step(0, no{}, no{}, no{});
+  int kt = 1;
+  for (; kt + 2 < KT; ++kt) stage_step(kt, yes{}, yes{}, yes{});
+  if (kt == KT - 2) {
+    stage_step(kt, yes{}, no{}, yes{});
+    ++kt;
+  }
+  if (kt == KT - 1) stage_step(kt, no{}, no{}, no{});
+}
+
 // K loop and epilogue of one wave, for LIVE (compile-time) token sub-tiles of 32 rows that
 // hold data. Every wave of a block runs the same number of K steps and barriers; waves
 // with fewer live sub-tiles skip MFMAs, not loads.
@@ -431,6 +587,8 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
 
   if constexpr (BT == 256 && BK == 32 && NST >= 3) {
     kloop_pipelined<LIVE, TR>(acc, lds, dp, K, wave, aoff, boff, swz_l, khalf);
+  } else if constexpr (BT == 256 && BK == 64 && NST == 2 && !TR) {
+    kloop_wide<LIVE>(acc, lds, dp, K, wave, aoff, boff, swz_l, khalf);
   } else {
     // Ring of NST LDS stages, DMA running NST-1 stages ahead of the MFMAs. At step kt the
     // stage kt is complete once at most (NST-2) later stages of DMA are still in flight.
@@ -1106,6 +1264,49 @@ GroupedWs carve(const Shape& s, void* ws) {
 
 }  // namespace
 
+#ifdef MOE_GEMM_WIDE_TU
+// Built a second time with K stages of 64 (grouped_mlp_wide.hip): this translation unit
+// provides the launches that read weights stored [N][K] (gated, gated with both products
+// saved, plain, plain split-K) of those kernels only. `args`
+// is the caller's GemmArgs (the same definition, from the same source).
+hipError_t launch_gemm_wide(int mode, unsigned grid, const void* args, hipStream_t st) {
+  const GemmArgs& a = *static_cast<const GemmArgs*>(args);
+  const dim3 gd(grid), bd(kThreads);
+  switch (mode) {
+    case kGemmGated: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGated, kBT>), gd, bd, 0, st, a); break;
+    case kGemmPlain: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kBT>), gd, bd, 0, st, a); break;
+    case kGemmPlainSplit: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainSplit, kBT>), gd, bd, 0, st, a); break;
+    case kGemmGatedSave: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGatedSave, kBT>), gd, bd, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+#else
+hipError_t launch_gemm_wide(int mode, unsigned grid, const void* args, hipStream_t st);
+
+// The launches that read weights stored [N][K] use the kernels with K stages of 64 (measured
+// on the DeepSeek-shaped, Mixtral-shaped and fine-grained layers: step 14.17 -> 13.71,
+// 2.92 -> 2.81 and 0.929 -> 0.916 ms, both grouped launches faster); 0 keeps them on this
+// unit's stages of 32.
+#ifndef MOE_GEMM_FWD_WIDE
+#define MOE_GEMM_FWD_WIDE 1
+#endif
+namespace {
+// One launch of the persistent grouped GEMM in a mode that reads weights stored [N][K].
+hipError_t launch_forward(int mode, int64_t grid, const GemmArgs& a, hipStream_t st) {
+  if (MOE_GEMM_FWD_WIDE) return launch_gemm_wide(mode, static_cast<unsigned>(grid), &a, st);
+  const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
+  switch (mode) {
+    case kGemmGated: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGated, kBT>), gd, bd, 0, st, a); break;
+    case kGemmPlain: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kBT>), gd, bd, 0, st, a); break;
+    case kGemmPlainSplit: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainSplit, kBT>), gd, bd, 0, st, a); break;
+    case kGemmGatedSave: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGatedSave, kBT>), gd, bd, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
 float* small_m_partials(const Shape& s, void* ws) { return carve(s, ws).part; }
 
 int large_down_splits(const Shape& s) {
@@ -1204,12 +1405,12 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
   switch (L.mode) {
-    case kGemmGated: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGated, kBT>), gd, bd, 0, st, a); break;
-    case kGemmPlain: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kBT>), gd, bd, 0, st, a); break;
-    case kGemmGatedSave: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGatedSave, kBT>), gd, bd, 0, st, a); break;
+    case kGemmGated:
+    case kGemmPlain:
+    case kGemmGatedSave:
+    case kGemmPlainSplit: return launch_forward(L.mode, grid, a, st);
     case kGemmDgradGather: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmDgradGather, kBT>), gd, bd, 0, st, a); break;
     case kGemmWgrad: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmWgrad, kBT>), gd, bd, 0, st, a); break;
-    case kGemmPlainSplit: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainSplit, kBT>), gd, bd, 0, st, a); break;
     case kGemmDgrad: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmDgrad, kBT>), gd, bd, 0, st, a); break;
     case kGemmDgradSplit: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmDgradSplit, kBT>), gd, bd, 0, st, a); break;
     default: return hipErrorInvalidValue;
@@ -1259,8 +1460,9 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     const int n_cu = cu_count();
     const int64_t g1 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb);
     timing_begin(MOE_KERNEL_GATE_UP, st);
-    hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGated, kBT>), dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0, st, a);
+    hipError_t le = launch_forward(kGemmGated, g1, a, st);
     timing_end(MOE_KERNEL_GATE_UP, st);
+    if (le != hipSuccess) return le;
     // launch 2: y = h Wd
     a.sorted_slot = nullptr;
     a.in_r = static_cast<const bf16_t*>(w.h);
@@ -1286,13 +1488,9 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.part_rows = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
     const int64_t g2 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb * sp);
     timing_begin(MOE_KERNEL_DOWN, st);
-    if (sp > 1)
-      hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainSplit, kBT>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0,
-                         st, a);
-    else
-      hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kBT>), dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, st,
-                         a);
+    le = launch_forward(sp > 1 ? kGemmPlainSplit : kGemmPlain, g2, a, st);
     timing_end(MOE_KERNEL_DOWN, st);
+    if (le != hipSuccess) return le;
     if (sp > 1 && y_perm != nullptr) return launch_split_reduce(s, w.part, sp, offsets, y_perm, y_shared, st);
   } else {
     GemmArgsF32 a{};
@@ -1341,5 +1539,7 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
   }
   return hipGetLastError();
 }
+
+#endif  // MOE_GEMM_WIDE_TU
 
 }  // namespace moe
