@@ -1284,17 +1284,22 @@ hipError_t launch_gemm_wide(int mode, unsigned grid, const void* args, hipStream
 #else
 hipError_t launch_gemm_wide(int mode, unsigned grid, const void* args, hipStream_t st);
 
-// The launches that read weights stored [N][K] use the kernels with K stages of 64 (measured
-// on the DeepSeek-shaped, Mixtral-shaped and fine-grained layers: step 14.17 -> 13.71,
-// 2.92 -> 2.81 and 0.929 -> 0.916 ms, both grouped launches faster); 0 keeps them on this
-// unit's stages of 32.
+// The launches that read weights stored [N][K] use the kernels with K stages of 64 when the
+// routed groups average at least kWideMinRows rows (measured on the DeepSeek-shaped,
+// Mixtral-shaped and fine-grained layers: step 14.17 -> 13.71, 2.92 -> 2.81 and 0.929 ->
+// 0.916 ms, both grouped launches faster). Smaller groups leave the tiles mostly empty and
+// the launch bound by its weight stream, which the deeper ring of stages of 32 keeps further
+// ahead (Mixtral-shaped T = 64, 16 rows an expert: gated launch 347 against 390 us). 0 keeps
+// every launch on this unit's stages of 32.
 #ifndef MOE_GEMM_FWD_WIDE
 #define MOE_GEMM_FWD_WIDE 1
 #endif
 namespace {
+constexpr int64_t kWideMinRows = 128;
+bool use_wide(int64_t T, int k, int E) { return MOE_GEMM_FWD_WIDE && T * k >= kWideMinRows * E; }
 // One launch of the persistent grouped GEMM in a mode that reads weights stored [N][K].
-hipError_t launch_forward(int mode, int64_t grid, const GemmArgs& a, hipStream_t st) {
-  if (MOE_GEMM_FWD_WIDE) return launch_gemm_wide(mode, static_cast<unsigned>(grid), &a, st);
+hipError_t launch_forward(int mode, int64_t grid, const GemmArgs& a, hipStream_t st, bool wide) {
+  if (wide) return launch_gemm_wide(mode, static_cast<unsigned>(grid), &a, st);
   const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
   switch (mode) {
     case kGemmGated: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGated, kBT>), gd, bd, 0, st, a); break;
@@ -1408,7 +1413,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t st) {
     case kGemmGated:
     case kGemmPlain:
     case kGemmGatedSave:
-    case kGemmPlainSplit: return launch_forward(L.mode, grid, a, st);
+    case kGemmPlainSplit: return launch_forward(L.mode, grid, a, st, use_wide(L.T, L.k, L.E));
     case kGemmDgradGather: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmDgradGather, kBT>), gd, bd, 0, st, a); break;
     case kGemmWgrad: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmWgrad, kBT>), gd, bd, 0, st, a); break;
     case kGemmDgrad: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmDgrad, kBT>), gd, bd, 0, st, a); break;
@@ -1460,7 +1465,8 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     const int n_cu = cu_count();
     const int64_t g1 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb);
     timing_begin(MOE_KERNEL_GATE_UP, st);
-    hipError_t le = launch_forward(kGemmGated, g1, a, st);
+    const bool wide = use_wide(s.T, s.k, s.E);
+    hipError_t le = launch_forward(kGemmGated, g1, a, st, wide);
     timing_end(MOE_KERNEL_GATE_UP, st);
     if (le != hipSuccess) return le;
     // launch 2: y = h Wd
@@ -1488,7 +1494,7 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.part_rows = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
     const int64_t g2 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb * sp);
     timing_begin(MOE_KERNEL_DOWN, st);
-    le = launch_forward(sp > 1 ? kGemmPlainSplit : kGemmPlain, g2, a, st);
+    le = launch_forward(sp > 1 ? kGemmPlainSplit : kGemmPlain, g2, a, st, wide);
     timing_end(MOE_KERNEL_DOWN, st);
     if (le != hipSuccess) return le;
     if (sp > 1 && y_perm != nullptr) return launch_split_reduce(s, w.part, sp, offsets, y_perm, y_shared, st);
