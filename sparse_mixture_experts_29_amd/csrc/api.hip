@@ -562,8 +562,8 @@ moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, const voi
                            sh ? sh->w_gate : nullptr, sh ? sh->w_up : nullptr, sh ? sh->w_down : nullptr, nullptr,
                            nullptr, w.grouped_ws, st, sc);
   if (e == hipSuccess)
-    e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false), w.pos, w.gate,
-                                y, st);
+    e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false, true), w.pos,
+                                w.gate, y, st);
   return hip_status(e);
 }
 

@@ -101,7 +101,7 @@ constexpr int kSmallMMaxRows = 64;
 constexpr int kSmallMRowsPerExpert = 8;
 bool small_m_fits(const Shape& s);
 bool use_small_m(const Shape& s);
-int small_m_splits(const Shape& s, bool gated);
+int small_m_splits(const Shape& s, bool gated, bool fp8 = false);
 // K splits of the tiled down launch (1 or 2), from the widths only: a long K against a narrow
 // output leaves few tiles per CU, and the last, partly filled round of tiles then dominates
 int large_down_splits(const Shape& s);

@@ -17,14 +17,17 @@
 //                 them in split order and applies silu * mul;
 //   down launch:  split-K partial sums of h Wd in fp32, reduced in a fixed order by a
 //                 second kernel (deterministic, no atomics).
-// Work units = (token half, group, K split, 16-column chunk); units of empty groups exit at
-// once. K splits keep the units small, so the last, partly filled round of waves is short.
+// Work units = (token half, group slot, K split, 16-column chunk), where the group slots are
+// the routed experts that hold rows (found on the device from the offsets) and then the
+// shared experts, so the grid covers only what a batch of T tokens can touch (min(E, T*k)
+// routed experts). K splits keep the units small, so the last, partly filled round of waves
+// is short.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;  // 4 waves, one unit each
+constexpr int kThreads = 256;  // at most 4 waves a block, one unit each
 
 struct SmallArgs {
   const bf16_t* in_r;          // routed input rows: x [T][K] (gather) or h [max_kept][K]
@@ -45,6 +48,7 @@ struct SmallArgs {
   int N_r, K_r, N_s, K_s;
   int E, k, T, n_shared;
   int n_chunks;                // 16-column chunks of the widest group
+  int r_slots;                 // routed group slots: min(E, T*k), the most experts a batch can touch
   int splits;                  // K splits; gated with 1 split writes h directly
   int halves;                  // waves per (group, split, chunk), each NGW token groups
   int fw;                      // gated partials: row stride is 2*fw (fw = widest N)
@@ -336,6 +340,41 @@ __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const void* w0,
   }
 }
 
+// The n-th (from 0) routed group holding rows, by increasing expert index, with its first
+// row and row count; g = -1 if fewer than n+1 groups hold rows. Wave-uniform: every lane
+// takes part in the ballots. The offsets of up to 256 experts are loaded at once, so finding
+// the group costs one memory round trip, as reading a known group's offsets does.
+struct GroupRows {
+  int g, r0, M;
+};
+__device__ __forceinline__ GroupRows nth_active_group(const int32_t* __restrict__ offsets, int E, int n, int lane) {
+  int before = 0;
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    int lo[4], hi[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {  // unconditional loads (clamped): no branch around them
+      const int e = e0 + 64 * c + lane;
+      lo[c] = offsets[min(e, E)];
+      hi[c] = offsets[min(e + 1, E)];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool act = hi[c] > lo[c];
+      const uint64_t m = __ballot(act);
+      const int cnt = __popcll(m);
+      if (n < before + cnt) {
+        const int rank = __popcll(m & ((uint64_t{1} << lane) - 1));
+        const uint64_t hit = __ballot(act && rank == n - before);
+        const int l = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(hit)) - 1);
+        const int r0 = __builtin_amdgcn_readlane(lo[c], l);
+        return GroupRows{e0 + 64 * c + l, r0, __builtin_amdgcn_readlane(hi[c], l) - r0};
+      }
+      before += cnt;
+    }
+  }
+  return GroupRows{-1, 0, 0};
+}
+
 // NGW: token groups of 16 per wave (1 or 2, so the 3-deep ring fits the register file). A
 // group with more rows than NGW*16 is covered by `halves` passes, one per NGW token groups.
 // The half is the slowest unit index: in a typical small batch every group fits one half,
@@ -344,29 +383,36 @@ template <bool GATED, int NGW, bool FP8, int CPW = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void small_m_kernel(SmallArgs a) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (readfirstlane): everything derived from the unit stays in scalar registers
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // unit = (half, group, split, chunk) with the chunk fastest: the waves of a block share a
-  // group, so blocks of empty groups retire at once
-  const int G = a.E + a.n_shared;
+  // blocks of 1 or 4 waves (blockDim.x 64 or 256)
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // unit = (half, group slot, split, chunk) with the chunk fastest: the waves of a block share
+  // a group. Slots 0 .. r_slots-1 are the routed experts that hold rows, in increasing order
+  // (at most min(E, T*k) of them), so no block is launched for an expert the batch does not
+  // touch; the shared experts follow.
+  const int GS = a.r_slots + a.n_shared;
   const int nc = static_cast<int>(unit % a.n_chunks);
   int64_t rest = unit / a.n_chunks;
   const int split = static_cast<int>(rest % a.splits);
   rest /= a.splits;
-  const int g = static_cast<int>(rest % G);
-  const int half = static_cast<int>(rest / G);
+  const int gs = static_cast<int>(rest % GS);
+  const int half = static_cast<int>(rest / GS);
   if (half >= a.halves) return;
+  GroupRows gr{a.E + (gs - a.r_slots), 0, a.T};  // a shared expert: all T tokens
+  if (gs < a.r_slots) {
+    if (a.r_slots == a.E) {  // every expert has its slot (empty ones exit below)
+      gr.g = gs;
+      gr.r0 = a.offsets[gs];
+      gr.M = a.offsets[gs + 1] - gr.r0;
+    } else {
+      gr = nth_active_group(a.offsets, a.E, gs, lane);
+    }
+  }
+  const int g = gr.g;
+  if (g < 0) return;  // fewer experts hold rows than there are slots
   const bool shared = g >= a.E;
   const int gi = shared ? g - a.E : g;
-  int r0, M;
-  if (shared) {
-    r0 = 0;
-    M = a.T;
-  } else {
-    r0 = a.offsets[g];
-    M = a.offsets[g + 1] - r0;
-  }
-  r0 = __builtin_amdgcn_readfirstlane(r0);
-  M = __builtin_amdgcn_readfirstlane(M);
+  const int r0 = __builtin_amdgcn_readfirstlane(gr.r0);
+  const int M = __builtin_amdgcn_readfirstlane(gr.M);
   const int t0 = half * NGW;            // first token group of this wave
   const int ng = ((M + 15) >> 4) - t0;  // token groups left for it
   if (ng <= 0) return;
@@ -484,11 +530,21 @@ hipError_t launch_split_reduce(const Shape& s, const float* part, int splits, co
 
 // K splits per launch: enough (group, chunk, split) units that the tail of the launch (the
 // last, partly filled round of waves) is short, while each split keeps >= 1024 of K.
-constexpr int64_t kSmallMUnitsTarget = 8192;
+#ifndef MOE_SM_UNITS_TARGET
+#define MOE_SM_UNITS_TARGET 8192
+#endif
+constexpr int64_t kSmallMUnitsTarget = MOE_SM_UNITS_TARGET;
 // wave slots of one round: 256 CUs x 2 blocks of 4 waves (two waves per SIMD)
 constexpr int64_t kSmallMWaveSlots = 2048;
 
-int small_m_splits(const Shape& s, bool gated) {
+// Waves per block of a launch of `units` work units: a launch that fits one round of wave
+// slots takes blocks of one wave, so the dispatcher spreads its waves evenly over the CUs (a
+// single token's gated launch: 1792 waves, 7 a CU, where blocks of four leave some CUs
+// with eight and others with four; Mixtral-shaped T = 1: 85.0 -> 79.8 us); longer launches
+// keep blocks of four, which dispatch faster (T = 4, 16: 1-2% slower with blocks of one).
+int block_waves(int64_t units) { return units <= kSmallMWaveSlots ? 1 : 4; }
+
+int small_m_splits(const Shape& s, bool gated, bool fp8) {
   const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
   const int64_t units = static_cast<int64_t>(max_groups(s)) * ((gated ? fmax : s.d) / 16);
   auto fits = [&](int sp) {  // every group's K splits into multiples of 64, each >= 1024
@@ -500,6 +556,15 @@ int small_m_splits(const Shape& s, bool gated) {
   // a gated launch whose units all fit one round (one or two experts: a single token) runs
   // unsplit: no round tail to shorten, and no reduction launch
   if (gated && units <= kSmallMWaveSlots) return 1;
+  // a single token's down launch: every routed slot holds rows (the token's k experts), so
+  // the units are known exactly; take as many K splits as fill one round of wave slots (FP8
+  // weights: two 16-row chunks a wave). Mixtral-shaped T = 1: 4 splits instead of 8, down
+  // launch 47.9 -> 44.2 us; the FP8 down launch keeps its 8.
+  const int64_t real = fp8 ? units / 2 : units;
+  if (!gated && s.T == 1 && real <= kSmallMWaveSlots) {
+    while (real * 2 * sp <= kSmallMWaveSlots && sp < 16 && fits(2 * sp)) sp *= 2;
+    return sp;
+  }
   while (units * sp < kSmallMUnitsTarget && sp < 16 && fits(2 * sp)) sp *= 2;
   return sp;
 }
@@ -510,7 +575,8 @@ size_t small_m_ws_bytes(const Shape& s) {
   const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
   const int sg = small_m_splits(s, true);
   const size_t gated = sg > 1 ? static_cast<size_t>(sg) * rows_total * 2 * fmax * sizeof(float) : 0;
-  const size_t down = static_cast<size_t>(small_m_splits(s, false)) * rows_total * s.d * sizeof(float);
+  const int sd = std::max(small_m_splits(s, false, false), small_m_splits(s, false, true));
+  const size_t down = static_cast<size_t>(sd) * rows_total * s.d * sizeof(float);
   return align256(std::max(gated, down));
 }
 
@@ -528,7 +594,8 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   a.T = static_cast<int>(s.T);
   a.n_shared = s.n_shared;
   a.max_kept = s.max_kept;
-  const int G = s.E + s.n_shared;
+  a.r_slots = static_cast<int>(std::min<int64_t>(s.E, s.T * s.k));
+  const int G = a.r_slots + s.n_shared;  // group slots (experts that can hold rows)
   // gated: h = silu(x Wg) * (x Wu)
   a.in_r = static_cast<const bf16_t*>(x);
   a.in_s = static_cast<const bf16_t*>(x);
@@ -572,7 +639,8 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   a.s1_s = fp8.shared_up;
   units *= a.halves;
   timing_begin(MOE_KERNEL_GATE_UP, st);
-  hipLaunchKernelGGL(kern_g, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(kThreads), 0, st, a);
+  int wpb = block_waves(units);
+  hipLaunchKernelGGL(kern_g, dim3(static_cast<unsigned>((units + wpb - 1) / wpb)), dim3(64 * wpb), 0, st, a);
   timing_end(MOE_KERNEL_GATE_UP, st);
   const int64_t rows_total = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
   if (a.splits > 1) {
@@ -599,10 +667,11 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   a.N_s = s.d;
   a.K_s = s.f_s;
   a.n_chunks = s.d / (16 * cpw_d);
-  a.splits = small_m_splits(s, false);
+  a.splits = small_m_splits(s, false, f8);
   units = static_cast<int64_t>(G) * a.n_chunks * a.splits * a.halves;
   timing_begin(MOE_KERNEL_DOWN, st);
-  hipLaunchKernelGGL(kern_d, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(kThreads), 0, st, a);
+  wpb = block_waves(units);
+  hipLaunchKernelGGL(kern_d, dim3(static_cast<unsigned>((units + wpb - 1) / wpb)), dim3(64 * wpb), 0, st, a);
   timing_end(MOE_KERNEL_DOWN, st);
   if (y_perm == nullptr) return hipGetLastError();  // the caller combines from the partials
   const int64_t threads = rows_total * (s.d / 8);
