@@ -96,6 +96,12 @@ template <bool GATED, int NG, bool FP8>
 struct RingDepth<GATED, NG, FP8, 2> {
   static constexpr int v[2] = {GATED ? 2 : 3, GATED ? 2 : 3};
 };
+// four chunks per wave (FP8 down launch): a ring of two blocks at two token groups (three
+// spill), three at one
+template <bool GATED, int NG, bool FP8>
+struct RingDepth<GATED, NG, FP8, 4> {
+  static constexpr int v[2] = {NG == 2 ? 2 : 3, NG == 2 ? 2 : 3};
+};
 #define MOE_SM_RING(G, N, F, DEPTHS)          \
   template <>                                 \
   struct RingDepth<G, N, F> {                 \
@@ -544,6 +550,16 @@ constexpr int64_t kSmallMWaveSlots = 2048;
 // keep blocks of four, which dispatch faster (T = 4, 16: 1-2% slower with blocks of one).
 int block_waves(int64_t units) { return units <= kSmallMWaveSlots ? 1 : 4; }
 
+// 16-row chunks per wave of the down launch: one for bf16 weights; four for FP8 weights,
+// whose token rows (bf16 h) are then read once per 64 weight rows instead of 32, except for
+// a single token, whose launch then has too few waves (Mixtral-shaped, one box, A/B builds:
+// down launch T = 64 125 -> 105 us, T = 16 87.5 -> 86.2 us, T = 4 61.3 -> 56.4 us, but
+// T = 1 25.2 -> 25.9 us).
+int small_m_down_cpw(const Shape& s, bool fp8) {
+  if (!fp8) return 1;
+  return s.T > 1 ? 4 : 2;
+}
+
 int small_m_splits(const Shape& s, bool gated, bool fp8) {
   const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
   const int64_t units = static_cast<int64_t>(max_groups(s)) * ((gated ? fmax : s.d) / 16);
@@ -560,7 +576,7 @@ int small_m_splits(const Shape& s, bool gated, bool fp8) {
   // the units are known exactly; take as many K splits as fill one round of wave slots (FP8
   // weights: two 16-row chunks a wave). Mixtral-shaped T = 1: 4 splits instead of 8, down
   // launch 47.9 -> 44.2 us; the FP8 down launch keeps its 8.
-  const int64_t real = fp8 ? units / 2 : units;
+  const int64_t real = gated ? units : units / small_m_down_cpw(s, fp8);
   if (!gated && s.T == 1 && real <= kSmallMWaveSlots) {
     while (real * 2 * sp <= kSmallMWaveSlots && sp < 16 && fits(2 * sp)) sp *= 2;
     return sp;
@@ -613,13 +629,14 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   // FP8 weights: two 16-row chunks per wave, so each token-row fragment feeds both and the
   // token-row reads from L2 per code byte halve. The gated launch takes them with two token
   // groups per wave (T > 16; at one group halving the units costs more than it saves), the
-  // down launch always. Measured on the Mixtral-shaped layer (A/B builds, one box): T = 64
-  // gated 245 -> 203 us and down 168 -> 126 us; down T = 16 104 -> 87 us, T = 1 28 -> 25 us;
-  // the gated launch at T <= 16 and every bf16 launch lose with two chunks. The K splits are
-  // chosen on 16-column chunks either way.
+  // down launch always (four past a single token: small_m_down_cpw). Measured on the
+  // Mixtral-shaped layer (A/B builds, one box): T = 64 gated 245 -> 203 us and down 168 ->
+  // 126 us; down T = 16 104 -> 87 us, T = 1 28 -> 25 us; the gated launch at T <= 16 and every
+  // bf16 launch lose with two chunks. The K splits are chosen on 16-column chunks either way
+  // (but for a single token, see small_m_splits).
   const int groups16 = static_cast<int>((s.T + 15) / 16);
   const int cpw_g = f8 && groups16 > 1 ? 2 : 1;
-  const int cpw_d = f8 ? 2 : 1;
+  const int cpw_d = small_m_down_cpw(s, f8);
   a.n_chunks = fmax / (16 * cpw_g);
   a.splits = small_m_splits(s, true);
   a.fw = fmax;
@@ -631,7 +648,8 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   auto kern_g = f8 ? (ngw == 1 ? small_m_kernel<true, 1, true>
                                 : (cpw_g == 2 ? small_m_kernel<true, 2, true, 2> : small_m_kernel<true, 2, true>))
                   : (ngw == 1 ? small_m_kernel<true, 1, false> : small_m_kernel<true, 2, false>);
-  auto kern_d = f8 ? (ngw == 1 ? small_m_kernel<false, 1, true, 2> : small_m_kernel<false, 2, true, 2>)
+  auto kern_d = f8 ? (ngw == 1 ? (cpw_d == 4 ? small_m_kernel<false, 1, true, 4> : small_m_kernel<false, 1, true, 2>)
+                                : small_m_kernel<false, 2, true, 4>)  // T > 16: four chunks
                   : (ngw == 1 ? small_m_kernel<false, 1, false> : small_m_kernel<false, 2, false>);
   a.s0_r = fp8.gate;
   a.s1_r = fp8.up;
