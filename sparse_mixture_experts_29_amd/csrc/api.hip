@@ -401,11 +401,16 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
                                       w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
   if (use_small_m(s)) {
     // small batches: combine straight from the down launch's split-K partials (no y_perm
-    // round trip, one launch fewer; the same values as the staged calls)
+    // round trip, one launch fewer; the same values as the staged calls); a single token's
+    // down launch combines by itself
+    SmallCombine comb;
+    comb.pos = w.pos;
+    comb.gate = w.gate;
+    comb.y = y;
     if (e == hipSuccess)
       e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, w_gate, w_up, w_down, ws_gate, ws_up,
-                             ws_down, nullptr, nullptr, w.grouped_ws, st);
-    if (e == hipSuccess)
+                             ws_down, nullptr, nullptr, w.grouped_ws, st, Fp8Scales{}, comb);
+    if (e == hipSuccess && !small_m_combines(s, false))
       e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false), w.pos,
                                   w.gate, y, st);
     return hip_status(e);

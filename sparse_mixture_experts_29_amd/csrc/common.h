@@ -170,14 +170,25 @@ struct Fp8Scales {
   const float* shared_down = nullptr;
 };
 
+// The layer's combine inputs and output, for a down launch that also combines.
+struct SmallCombine {
+  const int32_t* pos = nullptr;
+  const float* gate = nullptr;
+  void* y = nullptr;
+};
+// Whether the down launch of a small-batch step also combines into y (a single token with
+// bf16 weights and few experts: small_m_down_combine_kernel), given comb.y.
+bool small_m_combines(const Shape& s, bool fp8);
+
 // y_perm == nullptr: stop after the down launch and leave the fp32 split-K partials in the
-// workspace (small_m_partials) for launch_combine_partials
+// workspace (small_m_partials) for launch_combine_partials, or, with comb.y set and
+// small_m_combines, write y itself
 hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t* sorted_slot,
                                     const int32_t* offsets, const void* wg, const void* wu,
                                     const void* wd, const void* swg, const void* swu,
                                     const void* swd, void* h, void* hs, float* part,
                                     void* y_perm, void* y_shared, hipStream_t st,
-                                    const Fp8Scales& fp8 = Fp8Scales{});
+                                    const Fp8Scales& fp8 = Fp8Scales{}, const SmallCombine& comb = SmallCombine{});
 // the down launch's partials [splits][max_kept + n_s*T][d] inside the grouped-MLP workspace
 float* small_m_partials(const Shape& s, void* grouped_ws);
 // y from the partials: each kept slot's row is summed over the splits in order and rounded
@@ -202,7 +213,7 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
                               const int32_t* offsets, const void* wg, const void* wu,
                               const void* wd, const void* swg, const void* swu, const void* swd,
                               void* y_perm, void* y_shared, void* ws, hipStream_t st,
-                              const Fp8Scales& fp8 = Fp8Scales{});
+                              const Fp8Scales& fp8 = Fp8Scales{}, const SmallCombine& comb = SmallCombine{});
 hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos,
                           const float* gate, const void* y_shared, void* y, hipStream_t st);
 

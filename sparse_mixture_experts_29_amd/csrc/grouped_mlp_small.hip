@@ -126,11 +126,14 @@ MOE_SM_RING(false, 2, true, MOE_SM_DF2)
 // multiplies of both chunks, halving the token-row reads per weight byte (which, at two token
 // groups per wave, are larger than the FP8 weight reads themselves); chunk c's rows start
 // c * 16 rows (cstride bytes) after chunk 0's.
-template <bool GATED, int NG, bool FP8, int CPW = 1>
+// LDSP (down launch only): the fp32 partial goes to lds_part (token row tok of the unit at
+// lds_part[tok * 16 * CPW + column - n0]) instead of the global partials.
+template <bool GATED, int NG, bool FP8, int CPW = 1, bool LDSP = false>
 __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const void* w0, const void* w1,
                                              const bf16_t* const (&xp)[2], int t0, int kbeg, int kend,
                                              int quad, int l16, int M, int r0, int gi, bool shared,
-                                             int N, int n0, int split, int64_t cstride = 0) {
+                                             int N, int n0, int split, int64_t cstride = 0,
+                                             float* lds_part = nullptr) {
   constexpr int NW = FP8 ? 2 : 4;  // 16-byte weight loads per lane per block and matrix
   constexpr int DW = RingDepth<GATED, NG, FP8, CPW>::v[0];
   constexpr int DX = RingDepth<GATED, NG, FP8, CPW>::v[1];
@@ -335,6 +338,9 @@ __device__ __forceinline__ void small_m_unit(const SmallArgs& a, const void* w0,
           pk.x = pack_bf16x2(silu_f32(acc0q[t][0]) * acc1q[t][0], silu_f32(acc0q[t][1]) * acc1q[t][1]);
           pk.y = pack_bf16x2(silu_f32(acc0q[t][2]) * acc1q[t][2], silu_f32(acc0q[t][3]) * acc1q[t][3]);
           *reinterpret_cast<uint2*>(op) = pk;
+        } else if (LDSP) {
+          *reinterpret_cast<float4*>(lds_part + tok * 16 * CPW + ncol - n0) =
+              make_float4(acc0q[t][0], acc0q[t][1], acc0q[t][2], acc0q[t][3]);
         } else {
           const int64_t prow = shared ? a.max_kept + static_cast<int64_t>(gi) * a.T + row : row;
           const int64_t rows_total = a.max_kept + static_cast<int64_t>(a.n_shared) * a.T;
@@ -385,24 +391,11 @@ __device__ __forceinline__ GroupRows nth_active_group(const int32_t* __restrict_
 // group with more rows than NGW*16 is covered by `halves` passes, one per NGW token groups.
 // The half is the slowest unit index: in a typical small batch every group fits one half,
 // and the blocks of the other halves exit at once instead of idling inside working blocks.
-template <bool GATED, int NGW, bool FP8, int CPW = 1>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void small_m_kernel(SmallArgs a) {
-  const int lane = threadIdx.x & 63;
-  // wave-uniform (readfirstlane): everything derived from the unit stays in scalar registers
-  // blocks of 1 or 4 waves (blockDim.x 64 or 256)
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // unit = (half, group slot, split, chunk) with the chunk fastest: the waves of a block share
-  // a group. Slots 0 .. r_slots-1 are the routed experts that hold rows, in increasing order
-  // (at most min(E, T*k) of them), so no block is launched for an expert the batch does not
-  // touch; the shared experts follow.
-  const int GS = a.r_slots + a.n_shared;
-  const int nc = static_cast<int>(unit % a.n_chunks);
-  int64_t rest = unit / a.n_chunks;
-  const int split = static_cast<int>(rest % a.splits);
-  rest /= a.splits;
-  const int gs = static_cast<int>(rest % GS);
-  const int half = static_cast<int>(rest / GS);
-  if (half >= a.halves) return;
+// One work unit (group slot gs, K split, 16*CPW-column chunk nc, token half) of a wave; all
+// indices wave-uniform. Returns without work for slots past the groups that hold rows.
+template <bool GATED, int NGW, bool FP8, int CPW, bool LDSP = false>
+__device__ __forceinline__ void small_m_run(const SmallArgs& a, int nc, int split, int gs, int half, int lane,
+                                            float* lds_part = nullptr) {
   GroupRows gr{a.E + (gs - a.r_slots), 0, a.T};  // a shared expert: all T tokens
   if (gs < a.r_slots) {
     if (a.r_slots == a.E) {  // every expert has its slot (empty ones exit below)
@@ -456,11 +449,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   const int64_t cstride = int64_t{16} * K * (FP8 ? 1 : 2);  // bytes between the chunks' rows
   if (NGW == 1 || ng <= 1)
-    small_m_unit<GATED, 1, FP8, CPW>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split,
-                                     cstride);
+    small_m_unit<GATED, 1, FP8, CPW, LDSP>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0,
+                                           split, cstride, lds_part);
   else
-    small_m_unit<GATED, 2, FP8, CPW>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0, split,
-                                     cstride);
+    small_m_unit<GATED, 2, FP8, CPW, LDSP>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0,
+                                           split, cstride, lds_part);
+}
+
+template <bool GATED, int NGW, bool FP8, int CPW = 1>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void small_m_kernel(SmallArgs a) {
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (readfirstlane): everything derived from the unit stays in scalar registers
+  // blocks of 1 or 4 waves (blockDim.x 64 or 256)
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // unit = (half, group slot, split, chunk) with the chunk fastest: the waves of a block share
+  // a group. Slots 0 .. r_slots-1 are the routed experts that hold rows, in increasing order
+  // (at most min(E, T*k) of them), so no block is launched for an expert the batch does not
+  // touch; the shared experts follow.
+  const int GS = a.r_slots + a.n_shared;
+  const int nc = static_cast<int>(unit % a.n_chunks);
+  int64_t rest = unit / a.n_chunks;
+  const int split = static_cast<int>(rest % a.splits);
+  rest /= a.splits;
+  const int gs = static_cast<int>(rest % GS);
+  const int half = static_cast<int>(rest / GS);
+  if (half >= a.halves) return;
+  small_m_run<GATED, NGW, FP8, CPW>(a, nc, split, gs, half, lane);
+}
+
+// A single token's down launch that also combines: block nc covers the 16-column chunk nc of
+// y, one wave per (group slot, K split) unit (at most 8). Each wave leaves its fp32 partial
+// in LDS; then 16 lanes form y exactly as the ordered split reduction and the combine do
+// (each kept slot's partials summed in split order and rounded to bf16, then gate-weighted
+// in slot order, then the shared experts added, one rounding to bf16), so the results are
+// those of the separate launches, bit for bit.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void small_m_down_combine_kernel(
+    SmallArgs a, const int32_t* __restrict__ pos, const float* __restrict__ gate, bf16_t* __restrict__ y) {
+  __shared__ float part[8][16];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nc = blockIdx.x;
+  const int gs = w / a.splits, split = w % a.splits;
+  small_m_run<false, 1, false, 1, true>(a, nc, split, gs, 0, lane, part[w]);
+  __syncthreads();
+  if (w != 0 || lane >= 16) return;
+  auto round_bf16 = [](float v) { return __uint_as_float(pack_bf16x2(v, 0.f) << 16); };
+  auto slot_sum = [&](int g) {  // the unit partials of group slot g, in split order
+    float v = 0.f;
+    for (int q = 0; q < a.splits; ++q) v += part[g * a.splits + q][lane];
+    return round_bf16(v);
+  };
+  float acc = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    // the token's slot j: its row in the grouped order, which for a single token is the
+    // group slot of its expert (every expert the token touches holds exactly that one row)
+    const int p = pos[j];
+    if (p < 0) continue;
+    acc = fmaf(gate[j], slot_sum(p), acc);
+  }
+  for (int sh = 0; sh < a.n_shared; ++sh) acc += slot_sum(a.r_slots + sh);
+  reinterpret_cast<uint16_t*>(y)[nc * 16 + lane] = static_cast<uint16_t>(pack_bf16x2(acc, 0.f) & 0xffffu);
 }
 
 // h = silu(sum of gate partials) * (sum of up partials), the sums over K splits in split
@@ -585,6 +633,15 @@ int small_m_splits(const Shape& s, bool gated, bool fp8) {
   return sp;
 }
 
+// The fused single-token down launch and combine (small_m_down_combine_kernel): bf16 weights,
+// one token, at most 8 (group, K split) waves a chunk, and at least one round of wave slots
+// over all chunks (otherwise the separate launches stream the weights faster).
+bool small_m_combines(const Shape& s, bool fp8) {
+  if (fp8 || s.T != 1 || s.dtype != MOE_BF16) return false;
+  const int64_t waves = (static_cast<int64_t>(max_groups(s))) * small_m_splits(s, false, false);
+  return waves <= 8 && waves * (s.d / 16) >= kSmallMWaveSlots;
+}
+
 size_t small_m_ws_bytes(const Shape& s) {
   if (!small_m_fits(s)) return 0;  // also sized when bf16 batches take the tiled path (FP8 cannot)
   const int64_t rows_total = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
@@ -600,7 +657,8 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
                                     const int32_t* offsets, const void* wg, const void* wu,
                                     const void* wd, const void* swg, const void* swu,
                                     const void* swd, void* h, void* hs, float* part,
-                                    void* y_perm, void* y_shared, hipStream_t st, const Fp8Scales& fp8) {
+                                    void* y_perm, void* y_shared, hipStream_t st, const Fp8Scales& fp8,
+                                    const SmallCombine& comb) {
   SmallArgs a{};
   const bool f8 = fp8.gate != nullptr;
   a.sorted_slot = sorted_slot;
@@ -687,6 +745,15 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   a.n_chunks = s.d / (16 * cpw_d);
   a.splits = small_m_splits(s, false, f8);
   units = static_cast<int64_t>(G) * a.n_chunks * a.splits * a.halves;
+  if (comb.y != nullptr && small_m_combines(s, f8)) {
+    // a single token: the down launch forms y itself, one block of G x splits waves a chunk
+    timing_begin(MOE_KERNEL_DOWN, st);
+    hipLaunchKernelGGL(small_m_down_combine_kernel, dim3(static_cast<unsigned>(a.n_chunks)),
+                       dim3(static_cast<unsigned>(64 * G * a.splits)), 0, st, a, comb.pos, comb.gate,
+                       static_cast<bf16_t*>(comb.y));
+    timing_end(MOE_KERNEL_DOWN, st);
+    return hipGetLastError();
+  }
   timing_begin(MOE_KERNEL_DOWN, st);
   wpb = block_waves(units);
   hipLaunchKernelGGL(kern_d, dim3(static_cast<unsigned>((units + wpb - 1) / wpb)), dim3(64 * wpb), 0, st, a);
