@@ -96,6 +96,25 @@ LayerWs layer_layout(const Shape& s, void* base) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The layer workspace's routing and permutation buffers, for a gated launch that routes a
+// single token itself (bf16 activations).
+RouteArgs route_args(const Shape& s, const void* x, const void* w_router, const float* bias, const LayerWs& w) {
+  RouteArgs r;
+  r.x = static_cast<const bf16_t*>(x);
+  r.w_router = static_cast<const bf16_t*>(w_router);
+  r.bias = bias;
+  r.idx = w.idx;
+  r.gate = w.gate;
+  r.counts = w.counts;
+  r.offsets = w.offsets;
+  r.sorted_slot = w.sorted_slot;
+  r.pos = w.pos;
+  r.drop = w.drop;
+  r.gating = s.gating;
+  r.capacity = s.capacity;
+  return r;
+}
+
 int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
 
 // K splits of the backward's dx launch (K = 2f, N = d): split while there are fewer than
@@ -397,24 +416,30 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   LayerWs w = layer_layout(s, ws);
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
-                                      w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
+  hipError_t e = hipSuccess;
   if (use_small_m(s)) {
     // small batches: combine straight from the down launch's split-K partials (no y_perm
     // round trip, one launch fewer; the same values as the staged calls); a single token's
     // down launch combines by itself
+    const RouteArgs route = route_args(s, x, w_router, router_bias, w);
+    const bool routes = small_m_routes(s, false);
+    if (!routes)
+      e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
+                               w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
     SmallCombine comb;
     comb.pos = w.pos;
     comb.gate = w.gate;
     comb.y = y;
     if (e == hipSuccess)
       e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, w_gate, w_up, w_down, ws_gate, ws_up,
-                             ws_down, nullptr, nullptr, w.grouped_ws, st, Fp8Scales{}, comb);
+                             ws_down, nullptr, nullptr, w.grouped_ws, st, Fp8Scales{}, comb, routes ? &route : nullptr);
     if (e == hipSuccess && !small_m_combines(s, false))
       e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false), w.pos,
                                   w.gate, y, st);
     return hip_status(e);
   }
+  e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
+                           w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
   const int sp = large_down_splits(s);
   if (sp > 1) {
     // split-K down launch: combine from its fp32 partials (the same sums and roundings as the
@@ -559,13 +584,17 @@ moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, const voi
   hipStream_t st = static_cast<hipStream_t>(stream);
   const moe_fp8_weights* sh = s.n_shared > 0 ? shared : nullptr;
   // the small-batch sequence of moe_layer_forward: the combine reads the down launch's
-  // split-K partials
-  hipError_t e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
-                                      w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
+  // split-K partials; a single token is routed inside the gated launch
+  const RouteArgs route = route_args(s, x, w_router, router_bias, w);
+  const bool routes = small_m_routes(s, true);
+  hipError_t e = hipSuccess;
+  if (!routes)
+    e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
+                             w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
   if (e == hipSuccess)
     e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, experts->w_gate, experts->w_up, experts->w_down,
                            sh ? sh->w_gate : nullptr, sh ? sh->w_up : nullptr, sh ? sh->w_down : nullptr, nullptr,
-                           nullptr, w.grouped_ws, st, sc);
+                           nullptr, w.grouped_ws, st, sc, SmallCombine{}, routes ? &route : nullptr);
   if (e == hipSuccess)
     e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false, true), w.pos,
                                 w.gate, y, st);

@@ -170,6 +170,26 @@ struct Fp8Scales {
   const float* shared_down = nullptr;
 };
 
+// A single token's routing inputs and outputs (the route + permute launch's), for a gated
+// launch that routes the token itself.
+struct RouteArgs {
+  const bf16_t* x = nullptr;
+  const bf16_t* w_router = nullptr;
+  const float* bias = nullptr;
+  int32_t* idx = nullptr;
+  float* gate = nullptr;
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* sorted_slot = nullptr;
+  int32_t* pos = nullptr;
+  uint8_t* drop = nullptr;
+  int gating = 0;
+  int64_t capacity = -1;
+};
+// Whether a small-batch step's gated launch routes the batch itself (FP8 expert weights, a
+// single token, bf16 activations, E <= 8, its units within 8 waves per CU): then no route launch.
+bool small_m_routes(const Shape& s, bool fp8);
+
 // The layer's combine inputs and output, for a down launch that also combines.
 struct SmallCombine {
   const int32_t* pos = nullptr;
@@ -188,7 +208,8 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
                                     const void* wd, const void* swg, const void* swu,
                                     const void* swd, void* h, void* hs, float* part,
                                     void* y_perm, void* y_shared, hipStream_t st,
-                                    const Fp8Scales& fp8 = Fp8Scales{}, const SmallCombine& comb = SmallCombine{});
+                                    const Fp8Scales& fp8 = Fp8Scales{}, const SmallCombine& comb = SmallCombine{},
+                                    const RouteArgs* route = nullptr);
 // the down launch's partials [splits][max_kept + n_s*T][d] inside the grouped-MLP workspace
 float* small_m_partials(const Shape& s, void* grouped_ws);
 // y from the partials: each kept slot's row is summed over the splits in order and rounded
@@ -213,7 +234,8 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
                               const int32_t* offsets, const void* wg, const void* wu,
                               const void* wd, const void* swg, const void* swu, const void* swd,
                               void* y_perm, void* y_shared, void* ws, hipStream_t st,
-                              const Fp8Scales& fp8 = Fp8Scales{}, const SmallCombine& comb = SmallCombine{});
+                              const Fp8Scales& fp8 = Fp8Scales{}, const SmallCombine& comb = SmallCombine{},
+                              const RouteArgs* route = nullptr);
 hipError_t launch_combine(const Shape& s, const void* y_perm, const int32_t* pos,
                           const float* gate, const void* y_shared, void* y, hipStream_t st);
 

@@ -1427,11 +1427,11 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
                               const int32_t* offsets, const void* wg, const void* wu,
                               const void* wd, const void* swg, const void* swu, const void* swd,
                               void* y_perm, void* y_shared, void* ws, hipStream_t st, const Fp8Scales& fp8,
-                              const SmallCombine& comb) {
+                              const SmallCombine& comb, const RouteArgs* route) {
   GroupedWs w = carve(s, ws);
   if (use_small_m(s) || (fp8.gate && small_m_fits(s)))
     return launch_grouped_mlp_small(s, x, sorted_slot, offsets, wg, wu, wd, swg, swu, swd, w.h, w.hs,
-                                    w.part, y_perm, y_shared, st, fp8, comb);
+                                    w.part, y_perm, y_shared, st, fp8, comb, route);
   if (fp8.gate) return hipErrorInvalidValue;  // FP8 weights: weight-streaming path only
   const int bm = tile_rows(s);
   const int64_t mb = m_tile_bound(s);

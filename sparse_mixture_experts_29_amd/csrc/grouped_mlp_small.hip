@@ -23,6 +23,7 @@
 // routed experts). K splits keep the units small, so the last, partly filled round of waves
 // is short.
 #include "common.h"
+#include "route_block.h"
 
 namespace moe {
 namespace {
@@ -391,21 +392,12 @@ __device__ __forceinline__ GroupRows nth_active_group(const int32_t* __restrict_
 // group with more rows than NGW*16 is covered by `halves` passes, one per NGW token groups.
 // The half is the slowest unit index: in a typical small batch every group fits one half,
 // and the blocks of the other halves exit at once instead of idling inside working blocks.
-// One work unit (group slot gs, K split, 16*CPW-column chunk nc, token half) of a wave; all
-// indices wave-uniform. Returns without work for slots past the groups that hold rows.
-template <bool GATED, int NGW, bool FP8, int CPW, bool LDSP = false>
-__device__ __forceinline__ void small_m_run(const SmallArgs& a, int nc, int split, int gs, int half, int lane,
-                                            float* lds_part = nullptr) {
-  GroupRows gr{a.E + (gs - a.r_slots), 0, a.T};  // a shared expert: all T tokens
-  if (gs < a.r_slots) {
-    if (a.r_slots == a.E) {  // every expert has its slot (empty ones exit below)
-      gr.g = gs;
-      gr.r0 = a.offsets[gs];
-      gr.M = a.offsets[gs + 1] - gr.r0;
-    } else {
-      gr = nth_active_group(a.offsets, a.E, gs, lane);
-    }
-  }
+// One work unit (group gr.g with rows [gr.r0, gr.r0 + gr.M) of the grouped order, K split,
+// 16*CPW-column chunk nc, token half) of a wave; all indices wave-uniform. ONE_TOKEN: the
+// batch is a single token, so every row gathers token 0 (no sorted_slot read).
+template <bool GATED, int NGW, bool FP8, int CPW, bool LDSP = false, bool ONE_TOKEN = false>
+__device__ __forceinline__ void small_m_exec(const SmallArgs& a, GroupRows gr, int nc, int split, int half,
+                                             int lane, float* lds_part = nullptr) {
   const int g = gr.g;
   if (g < 0) return;  // fewer experts hold rows than there are slots
   const bool shared = g >= a.E;
@@ -444,7 +436,7 @@ __device__ __forceinline__ void small_m_run(const SmallArgs& a, int nc, int spli
     if (shared)
       src = GATED ? r : static_cast<int64_t>(gi) * a.T + r;
     else
-      src = GATED ? a.sorted_slot[r] / a.k : r;
+      src = GATED ? (ONE_TOKEN ? 0 : a.sorted_slot[r] / a.k) : r;
     xp[t] = in + src * K;
   }
   const int64_t cstride = int64_t{16} * K * (FP8 ? 1 : 2);  // bytes between the chunks' rows
@@ -454,6 +446,24 @@ __device__ __forceinline__ void small_m_run(const SmallArgs& a, int nc, int spli
   else
     small_m_unit<GATED, 2, FP8, CPW, LDSP>(a, w0, w1, xp, t0, kbeg, kend, quad, l16, M, r0, gi, shared, N, n0,
                                            split, cstride, lds_part);
+}
+
+// The unit of group slot gs: its group found from the offsets (slots 0 .. r_slots-1 the
+// routed experts that hold rows, in increasing order; then the shared experts), then run.
+template <bool GATED, int NGW, bool FP8, int CPW, bool LDSP = false>
+__device__ __forceinline__ void small_m_run(const SmallArgs& a, int nc, int split, int gs, int half, int lane,
+                                            float* lds_part = nullptr) {
+  GroupRows gr{a.E + (gs - a.r_slots), 0, a.T};  // a shared expert: all T tokens
+  if (gs < a.r_slots) {
+    if (a.r_slots == a.E) {  // every expert has its slot (empty ones exit below)
+      gr.g = gs;
+      gr.r0 = a.offsets[gs];
+      gr.M = a.offsets[gs + 1] - gr.r0;
+    } else {
+      gr = nth_active_group(a.offsets, a.E, gs, lane);
+    }
+  }
+  small_m_exec<GATED, NGW, FP8, CPW, LDSP>(a, gr, nc, split, half, lane, lds_part);
 }
 
 template <bool GATED, int NGW, bool FP8, int CPW = 1>
@@ -509,6 +519,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
   for (int sh = 0; sh < a.n_shared; ++sh) acc += slot_sum(a.r_slots + sh);
   reinterpret_cast<uint16_t*>(y)[nc * 16 + lane] = static_cast<uint16_t>(pack_bf16x2(acc, 0.f) & 0xffffu);
+}
+
+// A single token's gated launch that routes the token itself: every block runs the block
+// router on it (the first 256 threads; the same code and order as the route launch, so the
+// same experts and gates), keeps its k choices in LDS, and block 0 also writes the routing
+// and the permutation for the launches that follow. Then each wave runs its unit: group slot
+// gs < k is the token's gs-th expert by increasing index, whose single row is row gs of the
+// grouped order; the shared experts follow. Saves the route launch and its gap per step.
+// Blocks of 256 to 512 threads (the block router's 256 and up to 4 more waves).
+template <int EMAX, int TB, bool FP8>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void small_m_routed_kernel(
+    SmallArgs a, RouteArgs r) {
+  __shared__ int sidx[64];
+  const bool first = blockIdx.x == 0;
+  router_small_e_block<bf16_t, EMAX, TB, true>(r.x, r.w_router, r.bias, r.idx, r.gate, nullptr, 1, a.K_r, a.E,
+                                               a.k, r.gating, 0, sidx, first);
+  __syncthreads();
+  if (first && threadIdx.x < 64)
+    permute_tiny_wave(sidx, a.k, a.E, r.capacity, a.max_kept, r.counts, r.offsets, r.sorted_slot, r.pos, r.drop);
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nc = unit % a.n_chunks;
+  const int rest = unit / a.n_chunks;
+  const int split = rest % a.splits;
+  const int gs = rest / a.splits;
+  if (gs >= a.r_slots + a.n_shared) return;  // past the units (the last block)
+  GroupRows gr{a.E + (gs - a.r_slots), 0, 1};
+  if (gs < a.r_slots) {
+    // lane j < k holds choice j; its rank among the k (distinct) experts is its group slot
+    const int e = lane < a.k ? sidx[lane] : 0x7fffffff;
+    int rank = 0;
+    for (int j = 0; j < a.k; ++j) rank += sidx[j] < e ? 1 : 0;
+    const uint64_t hit = __ballot(lane < a.k && rank == gs);
+    const int l = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(hit)) - 1);
+    gr = GroupRows{__builtin_amdgcn_readlane(e, l), gs, 1};
+  }
+  small_m_exec<true, 1, FP8, 1, false, true>(a, gr, nc, split, 0, lane);
 }
 
 // h = silu(sum of gate partials) * (sum of up partials), the sums over K splits in split
@@ -633,13 +680,23 @@ int small_m_splits(const Shape& s, bool gated, bool fp8) {
   return sp;
 }
 
+// FP8 weights only: measured on the Mixtral-shaped T = 1 layer (A/B builds, interleaved, one
+// box), the FP8 step went 0.0866 -> 0.0837 ms (the gated launch grows by 1 us, the route
+// launch goes), while the bf16 step went 0.1340 -> 0.1350 ms (its gated launch grows by 5.5
+// us: with bf16 weights the launch's blocks of seven waves stream slower than blocks of one).
+bool small_m_routes(const Shape& s, bool fp8) {
+  if (!fp8 || s.T != 1 || s.dtype != MOE_BF16 || s.E > 8 || s.k > s.E) return false;
+  // the gated launch's units (one split: a single token's gated units fit one round)
+  const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
+  const int64_t units = static_cast<int64_t>(max_groups(s)) * (fmax / 16);
+  return small_m_splits(s, true) == 1 && units <= 8LL * cu_count();
+}
+
 // The fused single-token down launch and combine (small_m_down_combine_kernel): bf16 weights,
-// one token, at most 8 (group, K split) waves a chunk, and at least one round of wave slots
-// over all chunks (otherwise the separate launches stream the weights faster).
+// one token, at most 8 (group, K split) waves a chunk (one block).
 bool small_m_combines(const Shape& s, bool fp8) {
   if (fp8 || s.T != 1 || s.dtype != MOE_BF16) return false;
-  const int64_t waves = (static_cast<int64_t>(max_groups(s))) * small_m_splits(s, false, false);
-  return waves <= 8 && waves * (s.d / 16) >= kSmallMWaveSlots;
+  return static_cast<int64_t>(max_groups(s)) * small_m_splits(s, false, false) <= 8;
 }
 
 size_t small_m_ws_bytes(const Shape& s) {
@@ -658,7 +715,7 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
                                     const void* wd, const void* swg, const void* swu,
                                     const void* swd, void* h, void* hs, float* part,
                                     void* y_perm, void* y_shared, hipStream_t st, const Fp8Scales& fp8,
-                                    const SmallCombine& comb) {
+                                    const SmallCombine& comb, const RouteArgs* route) {
   SmallArgs a{};
   const bool f8 = fp8.gate != nullptr;
   a.sorted_slot = sorted_slot;
@@ -714,9 +771,19 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   a.s0_s = fp8.shared_gate;
   a.s1_s = fp8.shared_up;
   units *= a.halves;
-  timing_begin(MOE_KERNEL_GATE_UP, st);
   int wpb = block_waves(units);
-  hipLaunchKernelGGL(kern_g, dim3(static_cast<unsigned>((units + wpb - 1) / wpb)), dim3(64 * wpb), 0, st, a);
+  timing_begin(MOE_KERNEL_GATE_UP, st);
+  if (route != nullptr && small_m_routes(s, f8)) {
+    // a single token routed inside the launch: one block of 4 to 8 waves per CU (the block
+    // router needs 256 threads), so that every block's routing is shared by its waves and
+    // the waves spread evenly
+    const int64_t cus = cu_count();
+    const int w = std::max(4, static_cast<int>((units + cus - 1) / cus));
+    auto kern = f8 ? small_m_routed_kernel<8, 4, true> : small_m_routed_kernel<8, 4, false>;  // E <= 8
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((units + w - 1) / w)), dim3(64 * w), 0, st, a, *route);
+  } else {
+    hipLaunchKernelGGL(kern_g, dim3(static_cast<unsigned>((units + wpb - 1) / wpb)), dim3(64 * wpb), 0, st, a);
+  }
   timing_end(MOE_KERNEL_GATE_UP, st);
   const int64_t rows_total = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
   if (a.splits > 1) {

@@ -40,6 +40,11 @@ CASES = [
     R(fp8(configs.QWEN3_FINE), T=1, d_model=128, d_ff=64, n_experts=128, top_k=8),
     # capacity with drops, 4 rows per expert (the bf16 layer runs the same kernels)
     R(fp8(configs.QWEN3_FINE_CF), T=57, d_model=256, d_ff=128, n_experts=64, top_k=4),
+    # a single token with E <= 8, routed inside the gated launch: sigmoid gates with a shared
+    # expert and capacity 1; k = E
+    R(fp8(configs.DEEPSEEK_V3), T=1, d_model=256, d_ff=128, n_experts=8, top_k=3, d_ff_shared=128,
+      capacity_factor=1.0),
+    R(configs.mixtral_decode_fp8(1), d_model=192, d_ff=320, n_experts=4, top_k=4),
 ]
 
 

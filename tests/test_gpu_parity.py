@@ -81,6 +81,14 @@ EDGE = [
     # ... and E <= 8 with a partly filled 4-token block, bf16 and fp32
     R(configs.MIXTRAL_PREFILL, T=3, d_model=256, d_ff=128, n_experts=8, top_k=2),
     R(configs.TINY_FP32, T=2),
+    # a single token with E <= 8, routed inside the gated launch, whose down launch combines:
+    # sigmoid gates with a shared expert and capacity 1; k = E (every expert); one expert;
+    # three shared experts (more waves per output chunk than the combined down launch takes)
+    R(configs.DEEPSEEK_V3, T=1, d_model=256, d_ff=128, n_experts=8, top_k=3, d_ff_shared=128,
+      capacity_factor=1.0),
+    R(configs.MIXTRAL_PREFILL, T=1, d_model=192, d_ff=320, n_experts=4, top_k=4),
+    R(configs.MIXTRAL_PREFILL, T=1, d_model=128, d_ff=192, n_experts=1, top_k=1),
+    R(configs.DEEPSEEK_V3, T=1, d_model=128, d_ff=64, n_experts=6, top_k=6, n_shared=3, d_ff_shared=64),
 ]
 
 
