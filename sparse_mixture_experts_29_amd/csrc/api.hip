@@ -416,30 +416,24 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   LayerWs w = layer_layout(s, ws);
   if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
+  hipError_t e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
+                                      w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
   if (use_small_m(s)) {
     // small batches: combine straight from the down launch's split-K partials (no y_perm
     // round trip, one launch fewer; the same values as the staged calls); a single token's
     // down launch combines by itself
-    const RouteArgs route = route_args(s, x, w_router, router_bias, w);
-    const bool routes = small_m_routes(s, false);
-    if (!routes)
-      e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
-                               w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
     SmallCombine comb;
     comb.pos = w.pos;
     comb.gate = w.gate;
     comb.y = y;
     if (e == hipSuccess)
       e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, w_gate, w_up, w_down, ws_gate, ws_up,
-                             ws_down, nullptr, nullptr, w.grouped_ws, st, Fp8Scales{}, comb, routes ? &route : nullptr);
+                             ws_down, nullptr, nullptr, w.grouped_ws, st, Fp8Scales{}, comb);
     if (e == hipSuccess && !small_m_combines(s, false))
       e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false), w.pos,
                                   w.gate, y, st);
     return hip_status(e);
   }
-  e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
-                           w.sorted_slot, w.pos, w.drop, w.permute_ws, st);
   const int sp = large_down_splits(s);
   if (sp > 1) {
     // split-K down launch: combine from its fp32 partials (the same sums and roundings as the
