@@ -772,15 +772,31 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
             }
         }
       }
-      // read back: lane l takes chunk l % CHR of staged row it*(64/CHR) + l/CHR
+      // read back: lane l takes chunk l % CHR of staged row it*(64/CHR) + l/CHR, eight rows
+      // of instructions at a time (reads, then stores: one LDS latency per eight stores)
       constexpr int RPIT = 64 / CHR;  // staged rows per instruction
+      constexpr int NIT = SPP * 32 / RPIT;
+      constexpr int RB = NIT < 8 ? NIT : 8;
       const int rows = (min(LIVE, p0 + SPP) - p0) * 32;
   #pragma unroll
-      for (int it = 0; it < SPP * 32 / RPIT; ++it) {
+      for (int it0 = 0; it0 < NIT; it0 += RB) {
+        if (it0 * RPIT >= rows) break;
+        uint4 vb[RB];
+  #pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const int lr = (it0 + u) * RPIT + ln / CHR;
+          const int c = ln % CHR;
+          if ((it0 + u) * RPIT < rows)
+            vb[u] = *reinterpret_cast<const uint4*>(stg + lr * (CHR * 16) + ((c ^ (lr & (CHR - 1))) << 4));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int it = it0 + u;
         const int lr = it * RPIT + ln / CHR;
         if (it * RPIT >= rows) break;
         const int c = ln % CHR;
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + lr * (CHR * 16) + ((c ^ (lr & (CHR - 1))) << 4));
+        const uint4 v = vb[u];
         const int jt = p0 + lr / 32;  // this wave's sub-tile
         const int row = row0 + (2 * jt + wm) * 32 + (lr & 31);
         if (row >= row1) continue;
@@ -803,6 +819,7 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
           }
           if (n < N) *reinterpret_cast<uint4*>(op + col) = v;
         }
+      }
       }
     }
   }
@@ -1007,18 +1024,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
     }
   } else {
     dp.base = reinterpret_cast<const char*>(in);
+    int rr[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = row0 + (wave - 2) * WT + i * RPI + lrow;  // row0 + token row within the tile
+      rr[i] = r < row1 ? r : row0;
+    }
+    if (GATHER && !WGRAD && !shared) {
+      // gathered rows: all the slot loads first, so their latencies overlap (in source
+      // order the compiler waits for each before issuing the next)
+      uint32_t sl[IPW];
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) sl[i] = static_cast<uint32_t>(a.sorted_slot[rr[i]]);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t kk = static_cast<uint32_t>(a.k);
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) rr[i] = static_cast<int>(sl[i] / kk);
+    }
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int tr = (wave - 2) * WT + i * RPI + lrow;  // token row within the tile
-      int r = row0 + tr;
-      r = r < row1 ? r : row0;
-      int64_t src;
-      if (WGRAD)
-        src = r;
-      else if (shared)
-        src = GATHER ? r : static_cast<int64_t>(gi) * a.T + r;
-      else
-        src = GATHER ? a.sorted_slot[r] / a.k : r;
+      int64_t src = rr[i];
+      if (!WGRAD && shared && !GATHER) src += static_cast<int64_t>(gi) * a.T;
       const int c = (lane % CH) ^ swz(BW + tr);
       dp.off[i] = static_cast<uint32_t>(src * ldin * 2 + (c << 4));
     }
