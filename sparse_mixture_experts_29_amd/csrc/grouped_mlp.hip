@@ -101,6 +101,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // k0+{8..11} (lanes 32-63) at one segment: tr_swz sends those 8 rows to 8 distinct segments.
 __device__ __forceinline__ int tr_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
 
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -817,7 +818,10 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
             n = n0 + wn * 128 + c * 8;
             col = n;
           }
-          if (n < N) *reinterpret_cast<uint4*>(op + col) = v;
+          // non-temporal: each store writes whole 256-byte row segments that no later part of
+          // the launch reads (down launch 0.6-2% faster; the gated launch's 16-byte pieces of h
+          // were 6-14% slower with it, so they keep ordinary stores)
+          if (n < N) __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(op + col));
         }
       }
       }
