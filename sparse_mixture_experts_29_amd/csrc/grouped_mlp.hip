@@ -613,12 +613,13 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
     }
   }
 
-  // epilogue. Gated outputs (64 h columns a wave) and fp32 split partials are stored straight
-  // from the accumulators; the bf16 products of the plain, save and weight-gradient modes go
+  // epilogue. fp32 split partials are stored straight from the accumulators; bf16 products go
   // out through LDS (measured per tile: staging takes the plain epilogue from 15 k to 10 k
-  // cycles and the weight-gradient one from 21 k to 12 k, but costs the gated one 8% and the
-  // fp32 one 10% more).
-  constexpr bool STAGED = !F32 && (!GATED || SAVE);
+  // cycles and the weight-gradient one from 21 k to 12 k, but costs the fp32 one 10% more;
+  // for the gated launch's h it measured 8% slower while the read-back alternated LDS reads
+  // and stores, and 0.5-1% faster with the batched read-back and non-temporal stores:
+  // DeepSeek-shaped gated launch 8.44 -> 8.39 ms, Mixtral 1.703 -> 1.685 ms).
+  constexpr bool STAGED = !F32;
   if constexpr (!STAGED) {
     // epilogue. acc[i][j] register r of lane l: weight row (operand A) 8*(r/4) + 4*(l/32) + r%4
     // of sub-tile i, token row 32*(2j + wm) + l%32.
