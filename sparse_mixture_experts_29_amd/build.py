@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "router.hip", "permute.hip", "grouped_mlp.hip", "grouped_mlp_small.hip", "combine.hip",
-           "backward.hip", "pack.hip", "grouped_mlp_wide.hip"]
+           "backward.hip", "pack.hip", "grouped_mlp_wide.hip", "grouped_mlp_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -705,7 +705,7 @@ __device__ __forceinline__ void tile_loop(bf16_t* lds, const DmaPlan& dp, int K,
     constexpr int CHR = CW * ES / 16;                   // 16-byte chunks per staged row: 8, 16, 32
     constexpr int TJL = BT / 64;                        // token sub-tiles per wave
     constexpr int SPP = F32 ? (BT == 256 ? 2 : 1) : TJL;  // token sub-tiles per pass
-    constexpr int QUARTER = BT == 256 ? 32768 : 16384;  // bytes of the ring per wave
+    constexpr int QUARTER = BT == 256 ? 32768 : BT == 128 ? 16384 : 8192;  // bytes of the ring per wave
     static_assert(SPP * 32 * CHR * 16 <= QUARTER, "a pass fits the wave's quarter of the ring");
     static_assert(4 * QUARTER <= NST * (BW + BT) * BK * 2, "the quarters fit the ring");
     stage_barrier();  // every wave is done reading the last stage
@@ -1067,7 +1067,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, bf16_t* lds, int L,
   // live token sub-tiles of this wave: those of the tile's ceil(rows/32) that are 2j + wm
   const int sub = (row1 - row0 + 31) / 32;
   const int live = __builtin_amdgcn_readfirstlane(max(0, min(TJ, (sub - (wave >> 1) + 1) / 2)));
-  static_assert(TJ == 4 || TJ == 2, "token sub-tiles per wave");
+  static_assert(TJ == 4 || TJ == 2 || TJ == 1, "token sub-tiles per wave");
   if (live >= TJ)
     tile_loop<GATED, BT, TJ, SAVE, SPLIT, TR>(lds, dp, K, wave, lane, row0, row1, n0, N, out, out_row_base);
   else if (live == 0)
@@ -1264,10 +1264,30 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
 constexpr int kBT = 256;  // token rows per bf16 tile
 int tile_rows(const Shape& s) { return s.dtype == MOE_BF16 ? kBT : FBM; }
 
-int64_t m_tile_bound(const Shape& s) {
-  const int bm = tile_rows(s);
+// Decode-sized batches past the weight-streaming path (experts averaging at most 16 rows, and
+// shared experts seeing at most 64 tokens) run the forward launches on tiles of kDecodeBT token
+// rows (grouped_mlp_decode.hip): such launches only stream weights, and a 64-row token part
+// leaves the LDS to a deeper ring of weight stages (Mixtral-shaped T = 64: step 0.541 -> 0.536
+// ms, both launches 1% faster; a 3-stage ring with two blocks per CU was slower, 0.65 ms).
+// 0 keeps them on 256-row tiles.
+#ifndef MOE_GEMM_FWD_DECODE
+#define MOE_GEMM_FWD_DECODE 1
+#endif
+constexpr int kDecodeBT = 64;
+bool use_decode_tiles(const Shape& s) {
+  return MOE_GEMM_FWD_DECODE && s.dtype == MOE_BF16 && !use_small_m(s) && s.T * s.k <= 16 * static_cast<int64_t>(s.E) &&
+         (s.n_shared == 0 || s.T <= kDecodeBT);
+}
+// token rows per tile of the forward launches
+int fwd_tile_rows(const Shape& s) { return use_decode_tiles(s) ? kDecodeBT : tile_rows(s); }
+
+int64_t m_tile_bound_rows(const Shape& s, int bm) {
   return (s.max_kept + bm - 1) / bm + s.E + static_cast<int64_t>(s.n_shared) * ((s.T + bm - 1) / bm);
 }
+// m-tiles of the backward's launches (256-row tiles) and of the forward's (the tile table in
+// the grouped workspace holds the larger)
+int64_t m_tile_bound(const Shape& s) { return m_tile_bound_rows(s, tile_rows(s)); }
+int64_t fwd_m_tile_bound(const Shape& s) { return m_tile_bound_rows(s, fwd_tile_rows(s)); }
 
 struct GroupedWs {
   int32_t* tiles;
@@ -1280,7 +1300,7 @@ struct GroupedWs {
 GroupedWs carve(const Shape& s, void* ws) {
   char* p = static_cast<char*>(ws);
   GroupedWs w;
-  const int64_t mb = m_tile_bound(s);
+  const int64_t mb = fwd_m_tile_bound(s);
   w.tiles = reinterpret_cast<int32_t*>(p);
   p += align256(static_cast<size_t>(mb) * kTileEntries * sizeof(int32_t));
   w.n_tiles = reinterpret_cast<int32_t*>(p);
@@ -1296,7 +1316,22 @@ GroupedWs carve(const Shape& s, void* ws) {
 
 }  // namespace
 
-#ifdef MOE_GEMM_WIDE_TU
+#if defined(MOE_GEMM_DECODE_TU)
+// Built a third time with 64-row token tiles and a ring of 7 stages of 32 (grouped_mlp_decode.hip):
+// the forward launches (gated, plain, plain split-K) of decode-sized tiled batches, reached
+// through launch_gemm_decode with the caller's GemmArgs.
+hipError_t launch_gemm_decode(int mode, unsigned grid, const void* args, hipStream_t st) {
+  const GemmArgs& a = *static_cast<const GemmArgs*>(args);
+  const dim3 gd(grid), bd(kThreads);
+  switch (mode) {
+    case kGemmGated: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmGated, kDecodeBT>), gd, bd, 0, st, a); break;
+    case kGemmPlain: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlain, kDecodeBT>), gd, bd, 0, st, a); break;
+    case kGemmPlainSplit: hipLaunchKernelGGL((grouped_gemm_bf16<kGemmPlainSplit, kDecodeBT>), gd, bd, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+#elif defined(MOE_GEMM_WIDE_TU)
 // Built a second time with K stages of 64 (grouped_mlp_wide.hip): this translation unit
 // provides the launches that read weights stored [N][K] (gated, gated with both products
 // saved, plain, plain split-K) of those kernels only. `args`
@@ -1315,6 +1350,7 @@ hipError_t launch_gemm_wide(int mode, unsigned grid, const void* args, hipStream
 }
 #else
 hipError_t launch_gemm_wide(int mode, unsigned grid, const void* args, hipStream_t st);
+hipError_t launch_gemm_decode(int mode, unsigned grid, const void* args, hipStream_t st);
 
 // The launches that read weights stored [N][K] use the kernels with K stages of 64 when the
 // routed groups average at least kWideMinRows rows (measured on the DeepSeek-shaped,
@@ -1330,7 +1366,9 @@ namespace {
 constexpr int64_t kWideMinRows = 128;
 bool use_wide(int64_t T, int k, int E) { return MOE_GEMM_FWD_WIDE && T * k >= kWideMinRows * E; }
 // One launch of the persistent grouped GEMM in a mode that reads weights stored [N][K].
-hipError_t launch_forward(int mode, int64_t grid, const GemmArgs& a, hipStream_t st, bool wide) {
+hipError_t launch_forward(int mode, int64_t grid, const GemmArgs& a, hipStream_t st, bool wide,
+                          bool decode = false) {
+  if (decode) return launch_gemm_decode(mode, static_cast<unsigned>(grid), &a, st);
   if (wide) return launch_gemm_wide(mode, static_cast<unsigned>(grid), &a, st);
   const dim3 gd(static_cast<unsigned>(grid)), bd(kThreads);
   switch (mode) {
@@ -1363,7 +1401,7 @@ size_t large_split_ws_bytes(const Shape& s) {
 
 size_t grouped_ws_bytes(const Shape& s) {
   const size_t es = s.dtype == MOE_BF16 ? 2 : 4;
-  return align256(static_cast<size_t>(m_tile_bound(s)) * kTileEntries * sizeof(int32_t)) + 256 +
+  return align256(static_cast<size_t>(fwd_m_tile_bound(s)) * kTileEntries * sizeof(int32_t)) + 256 +
          align256(static_cast<size_t>(s.max_kept) * s.f * es) +
          align256(static_cast<size_t>(s.n_shared) * s.T * s.f_s * es) +
          std::max(small_m_ws_bytes(s), large_split_ws_bytes(s));
@@ -1465,8 +1503,9 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     return launch_grouped_mlp_small(s, x, sorted_slot, offsets, wg, wu, wd, swg, swu, swd, w.h, w.hs,
                                     w.part, y_perm, y_shared, st, fp8, comb, route);
   if (fp8.gate) return hipErrorInvalidValue;  // FP8 weights: weight-streaming path only
-  const int bm = tile_rows(s);
-  const int64_t mb = m_tile_bound(s);
+  const bool decode = use_decode_tiles(s);
+  const int bm = fwd_tile_rows(s);
+  const int64_t mb = fwd_m_tile_bound(s);
   int32_t* queues = w.n_tiles + 16;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, s.E, s.n_shared,
                      static_cast<int>(s.T), bm, w.tiles, w.n_tiles, queues);
@@ -1499,7 +1538,7 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     const int64_t g1 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb);
     timing_begin(MOE_KERNEL_GATE_UP, st);
     const bool wide = use_wide(s.T, s.k, s.E);
-    hipError_t le = launch_forward(kGemmGated, g1, a, st, wide);
+    hipError_t le = launch_forward(kGemmGated, g1, a, st, wide, decode);
     timing_end(MOE_KERNEL_GATE_UP, st);
     if (le != hipSuccess) return le;
     // launch 2: y = h Wd
@@ -1527,7 +1566,7 @@ hipError_t launch_grouped_mlp(const Shape& s, const void* x, const int32_t* sort
     a.part_rows = s.max_kept + static_cast<int64_t>(s.n_shared) * s.T;
     const int64_t g2 = std::min<int64_t>(n_cu, static_cast<int64_t>(a.n_tiles_n) * mb * sp);
     timing_begin(MOE_KERNEL_DOWN, st);
-    le = launch_forward(sp > 1 ? kGemmPlainSplit : kGemmPlain, g2, a, st, wide);
+    le = launch_forward(sp > 1 ? kGemmPlainSplit : kGemmPlain, g2, a, st, wide, decode);
     timing_end(MOE_KERNEL_DOWN, st);
     if (le != hipSuccess) return le;
     if (sp > 1 && y_perm != nullptr) return launch_split_reduce(s, w.part, sp, offsets, y_perm, y_shared, st);

@@ -41,6 +41,11 @@ CASES = [
     R(configs.MIXTRAL_PREFILL, T=600, d_model=256, d_ff=768),
     R(configs.DEEPSEEK_V3, T=300, d_model=128, d_ff=384, n_experts=16, top_k=4, d_ff_shared=256,
       capacity_factor=1.0),
+    # decode-sized tiled batches (at most 16 rows per expert on average) on 64-row token tiles:
+    # with a shared expert, with the split-K down launch, and ragged output widths
+    R(configs.DEEPSEEK_V3, T=48, d_model=256, d_ff=192, n_experts=16, top_k=4, d_ff_shared=320),
+    R(configs.DEEPSEEK_V3, T=60, d_model=128, d_ff=384, n_experts=16, top_k=4, d_ff_shared=256,
+      capacity_factor=1.0),
     # small batches wide enough to split K in both launches (a 64-wide tail inside each split)
     R(configs.mixtral_decode(4), d_model=2176, d_ff=2176),
     R(configs.DEEPSEEK_V3, T=8, d_model=2048, d_ff=2048, n_experts=16, top_k=4, d_ff_shared=2048),
@@ -249,6 +254,18 @@ def test_nan_logits_are_chosen_last_and_the_zeros_tie(E, k):
     want = np.array([4] + [e for e in range(E) if e != 4][: k - 1])
     assert (idx[rest] == want).all()
     assert (oracle.select_topk(bias[None, :].astype(np.float64), k)[0] == want).all()
+
+
+def test_decode_tiles_collapsed_router_spans_several_tiles():
+    """128 tokens, 16 experts, top-2 (8 rows per expert on average: 64-row token tiles), all
+    routed to experts 9 then 0: two groups of 128 rows, two tiles each, the rest empty."""
+    cfg = R(configs.MIXTRAL_PREFILL, T=128, d_model=256, d_ff=384, n_experts=16, top_k=2)
+    li = make_inputs(cfg)
+    li.w_router[:] = 0
+    li.router_bias = np.zeros(16, np.float32)
+    li.router_bias[9] = 4.0
+    dev = DeviceLayer(li)
+    P.check_layer_full(li, dev)
 
 
 def test_small_batch_collapsed_router_fills_four_token_groups():
