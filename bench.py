@@ -641,7 +641,10 @@ def main():
     # after the timed steps: the down launch in a pass of its own, then the clocks while the
     # layer runs
     _, _, down_ms = time_steps(dev.forward, K, 1, stream, kernel=binding.MOE_KERNEL_DOWN)
-    clocks = sample_clocks(dev.forward)
+    # counter runs (--copy-mib) skip it: under a counter profiler every child process loads the
+    # profiler, and the tool's own interpreter start (a script run through env) is then refused
+    clocks = (sample_clocks(dev.forward) if not args.copy_mib else
+              {"tool": "rocm-smi --showclocks --json", "samples": [], "error": "not sampled in counter runs (--copy-mib)"})
     flops_gate_up = 4.0 * cfg.d_model * cfg.d_ff * n_kept + 4.0 * cfg.d_model * cfg.d_ff_shared * cfg.T * cfg.n_shared
     flops_down = flops_gate_up / 2
     layer_flops = (cfg.expert_flops_per_pair() * n_kept + cfg.shared_flops() + cfg.router_flops())
