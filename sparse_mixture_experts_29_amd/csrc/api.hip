@@ -578,9 +578,14 @@ moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, const voi
   hipStream_t st = static_cast<hipStream_t>(stream);
   const moe_fp8_weights* sh = s.n_shared > 0 ? shared : nullptr;
   // the small-batch sequence of moe_layer_forward: the combine reads the down launch's
-  // split-K partials; a single token is routed inside the gated launch
+  // split-K partials; a single token is routed inside the gated launch, and its down launch
+  // combines by itself
   const RouteArgs route = route_args(s, x, w_router, router_bias, w);
   const bool routes = small_m_routes(s, true);
+  SmallCombine comb;
+  comb.pos = w.pos;
+  comb.gate = w.gate;
+  comb.y = y;
   hipError_t e = hipSuccess;
   if (!routes)
     e = launch_route_permute(s, x, w_router, router_bias, w.idx, w.gate, nullptr, w.counts, w.offsets,
@@ -588,8 +593,8 @@ moe_status moe_layer_forward_fp8(const moe_config* cfg, const void* x, const voi
   if (e == hipSuccess)
     e = launch_grouped_mlp(s, x, w.sorted_slot, w.offsets, experts->w_gate, experts->w_up, experts->w_down,
                            sh ? sh->w_gate : nullptr, sh ? sh->w_up : nullptr, sh ? sh->w_down : nullptr, nullptr,
-                           nullptr, w.grouped_ws, st, sc, SmallCombine{}, routes ? &route : nullptr);
-  if (e == hipSuccess)
+                           nullptr, w.grouped_ws, st, sc, comb, routes ? &route : nullptr);
+  if (e == hipSuccess && !small_m_combines(s, true))
     e = launch_combine_partials(s, small_m_partials(s, w.grouped_ws), small_m_splits(s, false, true), w.pos,
                                 w.gate, y, st);
   return hip_status(e);

@@ -196,8 +196,9 @@ struct SmallCombine {
   const float* gate = nullptr;
   void* y = nullptr;
 };
-// Whether the down launch of a small-batch step also combines into y (a single token with
-// bf16 weights and few experts: small_m_down_combine_kernel), given comb.y.
+// Whether the down launch of a small-batch step also combines into y (a single token with few
+// experts: small_m_down_combine_kernel, or small_m_down_combine_fp8_kernel with FP8 weights),
+// given comb.y.
 bool small_m_combines(const Shape& s, bool fp8);
 
 // y_perm == nullptr: stop after the down launch and leave the fp32 split-K partials in the

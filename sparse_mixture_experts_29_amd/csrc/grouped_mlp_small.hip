@@ -490,21 +490,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // A single token's down launch that also combines: block nc covers the 16-column chunk nc of
-// y, one wave per (group slot, K split) unit (at most 8). Each wave leaves its fp32 partial
+// y, one wave per (group slot, K split) unit (at most 8), bf16 or FP8 weights. Each wave leaves its fp32 partial
 // in LDS; then 16 lanes form y exactly as the ordered split reduction and the combine do
 // (each kept slot's partials summed in split order and rounded to bf16, then gate-weighted
 // in slot order, then the shared experts added, one rounding to bf16), so the results are
 // those of the separate launches, bit for bit.
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void small_m_down_combine_kernel(
-    SmallArgs a, const int32_t* __restrict__ pos, const float* __restrict__ gate, bf16_t* __restrict__ y) {
-  __shared__ float part[8][16];
+template <bool FP8, int CPW, int MAXW>
+__device__ __forceinline__ void small_m_down_combine(const SmallArgs& a, const int32_t* __restrict__ pos,
+                                                     const float* __restrict__ gate, bf16_t* __restrict__ y) {
+  __shared__ float part[MAXW][16 * CPW];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nc = blockIdx.x;
   const int gs = w / a.splits, split = w % a.splits;
-  small_m_run<false, 1, false, 1, true>(a, nc, split, gs, 0, lane, part[w]);
+  small_m_run<false, 1, FP8, CPW, true>(a, nc, split, gs, 0, lane, part[w]);
   __syncthreads();
-  if (w != 0 || lane >= 16) return;
+  if (w != 0 || lane >= 16 * CPW) return;
   auto round_bf16 = [](float v) { return __uint_as_float(pack_bf16x2(v, 0.f) << 16); };
   auto slot_sum = [&](int g) {  // the unit partials of group slot g, in split order
     float v = 0.f;
@@ -520,7 +521,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     acc = fmaf(gate[j], slot_sum(p), acc);
   }
   for (int sh = 0; sh < a.n_shared; ++sh) acc += slot_sum(a.r_slots + sh);
-  reinterpret_cast<uint16_t*>(y)[nc * 16 + lane] = static_cast<uint16_t>(pack_bf16x2(acc, 0.f) & 0xffffu);
+  reinterpret_cast<uint16_t*>(y)[nc * 16 * CPW + lane] = static_cast<uint16_t>(pack_bf16x2(acc, 0.f) & 0xffffu);
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void small_m_down_combine_kernel(
+    SmallArgs a, const int32_t* __restrict__ pos, const float* __restrict__ gate, bf16_t* __restrict__ y) {
+  small_m_down_combine<false, 1, 8>(a, pos, gate, y);
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void small_m_down_combine_fp8_kernel(
+    SmallArgs a, const int32_t* __restrict__ pos, const float* __restrict__ gate, bf16_t* __restrict__ y) {
+  small_m_down_combine<true, 1, 8>(a, pos, gate, y);
 }
 
 // A single token's gated launch that routes the token itself: every block runs the block
@@ -655,13 +666,15 @@ constexpr int64_t kSmallMWaveSlots = 2048;
 int block_waves(int64_t units) { return units <= kSmallMWaveSlots ? 1 : 4; }
 
 // 16-row chunks per wave of the down launch: one for bf16 weights; four for FP8 weights,
-// whose token rows (bf16 h) are then read once per 64 weight rows instead of 32, except for
-// a single token, whose launch then has too few waves (Mixtral-shaped, one box, A/B builds:
-// down launch T = 64 125 -> 105 us, T = 16 87.5 -> 86.2 us, T = 4 61.3 -> 56.4 us, but
-// T = 1 25.2 -> 25.9 us).
+// whose token rows (bf16 h) are then read once per 64 weight rows instead of 32 (Mixtral-shaped,
+// one box, A/B builds: down launch T = 64 125 -> 105 us, T = 16 87.5 -> 86.2 us, T = 4 61.3 ->
+// 56.4 us), except for a single token: one chunk a wave, so that its (expert, K split) units
+// of a 16-column chunk fit the one block of the down launch that also combines (two chunks
+// and 8 K splits ran the separate down launch 3 us faster, but the combine launch and its gap
+// cost more: FP8 T = 1 step 0.0869 -> 0.0846 ms).
 int small_m_down_cpw(const Shape& s, bool fp8) {
   if (!fp8) return 1;
-  return s.T > 1 ? 4 : 2;
+  return s.T > 1 ? 4 : 1;
 }
 
 int small_m_splits(const Shape& s, bool gated, bool fp8) {
@@ -677,9 +690,8 @@ int small_m_splits(const Shape& s, bool gated, bool fp8) {
   // unsplit: no round tail to shorten, and no reduction launch
   if (gated && units <= kSmallMWaveSlots) return 1;
   // a single token's down launch: every routed slot holds rows (the token's k experts), so
-  // the units are known exactly; take as many K splits as fill one round of wave slots (FP8
-  // weights: two 16-row chunks a wave). Mixtral-shaped T = 1: 4 splits instead of 8, down
-  // launch 47.9 -> 44.2 us; the FP8 down launch keeps its 8.
+  // the units are known exactly; take as many K splits as fill one round of wave slots.
+  // Mixtral-shaped T = 1: 4 splits instead of 8, down launch 47.9 -> 44.2 us.
   const int64_t real = gated ? units : units / small_m_down_cpw(s, fp8);
   if (!gated && s.T == 1 && real <= kSmallMWaveSlots) {
     while (real * 2 * sp <= kSmallMWaveSlots && sp < 16 && fits(2 * sp)) sp *= 2;
@@ -705,11 +717,11 @@ bool small_m_routes(const Shape& s, bool fp8) {
   return small_m_splits(s, true, true) == 1 && units <= 8LL * cu_count();
 }
 
-// The fused single-token down launch and combine (small_m_down_combine_kernel): bf16 weights,
-// one token, at most 8 (group, K split) waves a chunk (one block).
+// The fused single-token down launch and combine: one token, at most 8 (group, K split) waves
+// a 16-column chunk (small_m_down_combine_kernel, small_m_down_combine_fp8_kernel).
 bool small_m_combines(const Shape& s, bool fp8) {
-  if (fp8 || s.T != 1 || s.dtype != MOE_BF16) return false;
-  return static_cast<int64_t>(max_groups(s)) * small_m_splits(s, false, false) <= 8;
+  if (s.T != 1 || s.dtype != MOE_BF16) return false;
+  return static_cast<int64_t>(max_groups(s)) * small_m_splits(s, false, fp8) <= 8;
 }
 
 size_t small_m_ws_bytes(const Shape& s) {
@@ -759,8 +771,8 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   // groups per wave (T > 16; at one group halving the units costs more than it saves), the
   // down launch always (four past a single token: small_m_down_cpw). Measured on the
   // Mixtral-shaped layer (A/B builds, one box): T = 64 gated 245 -> 203 us and down 168 ->
-  // 126 us; down T = 16 104 -> 87 us, T = 1 28 -> 25 us; the gated launch at T <= 16 and every
-  // bf16 launch lose with two chunks. The K splits are chosen on 16-column chunks either way
+  // 126 us; down T = 16 104 -> 87 us; the gated launch at T <= 16 and every bf16 launch lose
+  // with two chunks. The K splits are chosen on 16-column chunks either way
   // (but for a single token, see small_m_splits).
   const int groups16 = static_cast<int>((s.T + 15) / 16);
   const int cpw_g = f8 && groups16 > 1 ? 2 : 1;
@@ -776,7 +788,7 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   auto kern_g = f8 ? (ngw == 1 ? small_m_kernel<true, 1, true>
                                 : (cpw_g == 2 ? small_m_kernel<true, 2, true, 2> : small_m_kernel<true, 2, true>))
                   : (ngw == 1 ? small_m_kernel<true, 1, false> : small_m_kernel<true, 2, false>);
-  auto kern_d = f8 ? (ngw == 1 ? (cpw_d == 4 ? small_m_kernel<false, 1, true, 4> : small_m_kernel<false, 1, true, 2>)
+  auto kern_d = f8 ? (ngw == 1 ? (cpw_d == 4 ? small_m_kernel<false, 1, true, 4> : small_m_kernel<false, 1, true, 1>)
                                 : small_m_kernel<false, 2, true, 4>)  // T > 16: four chunks
                   : (ngw == 1 ? small_m_kernel<false, 1, false> : small_m_kernel<false, 2, false>);
   a.s0_r = fp8.gate;
@@ -828,9 +840,9 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   if (comb.y != nullptr && small_m_combines(s, f8)) {
     // a single token: the down launch forms y itself, one block of G x splits waves a chunk
     timing_begin(MOE_KERNEL_DOWN, st);
-    hipLaunchKernelGGL(small_m_down_combine_kernel, dim3(static_cast<unsigned>(a.n_chunks)),
-                       dim3(static_cast<unsigned>(64 * G * a.splits)), 0, st, a, comb.pos, comb.gate,
-                       static_cast<bf16_t*>(comb.y));
+    hipLaunchKernelGGL(f8 ? small_m_down_combine_fp8_kernel : small_m_down_combine_kernel,
+                       dim3(static_cast<unsigned>(a.n_chunks)), dim3(static_cast<unsigned>(64 * G * a.splits)), 0, st,
+                       a, comb.pos, comb.gate, static_cast<bf16_t*>(comb.y));
     timing_end(MOE_KERNEL_DOWN, st);
     return hipGetLastError();
   }
