@@ -672,30 +672,47 @@ int block_waves(int64_t units) { return units <= kSmallMWaveSlots ? 1 : 4; }
 // of a 16-column chunk fit the one block of the down launch that also combines (two chunks
 // and 8 K splits ran the separate down launch 3 us faster, but the combine launch and its gap
 // cost more: FP8 T = 1 step 0.0869 -> 0.0846 ms).
+int single_token_down_splits(const Shape& s, int cpw);
+
 int small_m_down_cpw(const Shape& s, bool fp8) {
   if (!fp8) return 1;
-  return s.T > 1 ? 4 : 1;
+  if (s.T > 1) return 4;
+  // a single token: one chunk a wave where the down launch then combines (at most 8 units a
+  // chunk), else two
+  const int ts = single_token_down_splits(s, 1);
+  return ts > 0 && static_cast<int64_t>(max_groups(s)) * ts <= 8 ? 1 : 2;
+}
+
+// every group's K splits into sp parts that are multiples of 64, each >= 1024
+bool splits_fit(const Shape& s, bool gated, int sp) {
+  auto ok = [&](int K) { return K % sp == 0 && (K / sp) % 64 == 0 && K / sp >= 1024; };
+  if (gated) return ok(s.d);
+  return ok(s.f) && (s.n_shared == 0 || ok(s.f_s));
+}
+
+// K splits of a single token's down launch with cpw chunks a wave, or 0 when its units do not
+// fit one round of wave slots: every routed slot holds rows (the token's k experts), so the
+// units are known exactly; take as many K splits as fill one round. Mixtral-shaped T = 1: 4
+// splits instead of 8, down launch 47.9 -> 44.2 us.
+int single_token_down_splits(const Shape& s, int cpw) {
+  const int64_t real = static_cast<int64_t>(max_groups(s)) * (s.d / 16) / cpw;
+  if (real > kSmallMWaveSlots) return 0;
+  int sp = 1;
+  while (real * 2 * sp <= kSmallMWaveSlots && sp < 16 && splits_fit(s, false, 2 * sp)) sp *= 2;
+  return sp;
 }
 
 int small_m_splits(const Shape& s, bool gated, bool fp8) {
   const int fmax = s.n_shared && s.f_s > s.f ? s.f_s : s.f;
   const int64_t units = static_cast<int64_t>(max_groups(s)) * ((gated ? fmax : s.d) / 16);
-  auto fits = [&](int sp) {  // every group's K splits into multiples of 64, each >= 1024
-    auto ok = [&](int K) { return K % sp == 0 && (K / sp) % 64 == 0 && K / sp >= 1024; };
-    if (gated) return ok(s.d);
-    return ok(s.f) && (s.n_shared == 0 || ok(s.f_s));
-  };
+  auto fits = [&](int sp) { return splits_fit(s, gated, sp); };
   int sp = 1;
   // a gated launch whose units all fit one round (one or two experts: a single token) runs
   // unsplit: no round tail to shorten, and no reduction launch
   if (gated && units <= kSmallMWaveSlots) return 1;
-  // a single token's down launch: every routed slot holds rows (the token's k experts), so
-  // the units are known exactly; take as many K splits as fill one round of wave slots.
-  // Mixtral-shaped T = 1: 4 splits instead of 8, down launch 47.9 -> 44.2 us.
-  const int64_t real = gated ? units : units / small_m_down_cpw(s, fp8);
-  if (!gated && s.T == 1 && real <= kSmallMWaveSlots) {
-    while (real * 2 * sp <= kSmallMWaveSlots && sp < 16 && fits(2 * sp)) sp *= 2;
-    return sp;
+  if (!gated && s.T == 1) {
+    const int ts = single_token_down_splits(s, small_m_down_cpw(s, fp8));
+    if (ts > 0) return ts;
   }
   // expected routed experts touched by T tokens choosing k of E uniformly
   const double touched = s.E * (1.0 - std::pow(1.0 - static_cast<double>(s.k) / s.E, static_cast<double>(s.T)));
@@ -721,6 +738,7 @@ bool small_m_routes(const Shape& s, bool fp8) {
 // a 16-column chunk (small_m_down_combine_kernel, small_m_down_combine_fp8_kernel).
 bool small_m_combines(const Shape& s, bool fp8) {
   if (s.T != 1 || s.dtype != MOE_BF16) return false;
+  if (fp8 && small_m_down_cpw(s, true) != 1) return false;  // the fused FP8 kernel takes one chunk a wave
   return static_cast<int64_t>(max_groups(s)) * small_m_splits(s, false, fp8) <= 8;
 }
 
