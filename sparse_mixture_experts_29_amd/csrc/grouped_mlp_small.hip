@@ -806,7 +806,9 @@ hipError_t launch_grouped_mlp_small(const Shape& s, const void* x, const int32_t
   auto kern_g = f8 ? (ngw == 1 ? small_m_kernel<true, 1, true>
                                 : (cpw_g == 2 ? small_m_kernel<true, 2, true, 2> : small_m_kernel<true, 2, true>))
                   : (ngw == 1 ? small_m_kernel<true, 1, false> : small_m_kernel<true, 2, false>);
-  auto kern_d = f8 ? (ngw == 1 ? (cpw_d == 4 ? small_m_kernel<false, 1, true, 4> : small_m_kernel<false, 1, true, 1>)
+  auto kern_d = f8 ? (ngw == 1 ? (cpw_d == 4   ? small_m_kernel<false, 1, true, 4>
+                                  : cpw_d == 2 ? small_m_kernel<false, 1, true, 2>
+                                               : small_m_kernel<false, 1, true, 1>)
                                 : small_m_kernel<false, 2, true, 4>)  // T > 16: four chunks
                   : (ngw == 1 ? small_m_kernel<false, 1, false> : small_m_kernel<false, 2, false>);
   a.s0_r = fp8.gate;

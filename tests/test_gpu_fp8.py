@@ -45,6 +45,9 @@ CASES = [
     R(fp8(configs.DEEPSEEK_V3), T=1, d_model=256, d_ff=128, n_experts=8, top_k=3, d_ff_shared=128,
       capacity_factor=1.0),
     R(configs.mixtral_decode_fp8(1), d_model=192, d_ff=320, n_experts=4, top_k=4),
+    # a single token whose down units do not fit one block (8 experts and a shared one): two
+    # chunks a wave and the combine as a launch of its own
+    R(fp8(configs.DEEPSEEK_V3), T=1, d_model=2304, d_ff=256, n_experts=64, top_k=8, d_ff_shared=256),
 ]
 
 
