@@ -490,8 +490,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // A single token's down launch that also combines: block nc covers the 16-column chunk nc of
-// y, one wave per (group slot, K split) unit (at most 8), bf16 or FP8 weights. Each wave leaves its fp32 partial
-// in LDS; then 16 lanes form y exactly as the ordered split reduction and the combine do
+// y (16 * CPW columns), one wave per (group slot, K split) unit (at most 8), bf16 or FP8
+// weights. Each wave leaves its fp32 partial in LDS; then one lane per column forms y exactly
+// as the ordered split reduction and the combine do
 // (each kept slot's partials summed in split order and rounded to bf16, then gate-weighted
 // in slot order, then the shared experts added, one rounding to bf16), so the results are
 // those of the separate launches, bit for bit.
